@@ -1,0 +1,282 @@
+/*
+ * tk_oracle.c -- plain, slow CPU oracle for the per-token / per-group
+ * activation cast and for its fused SwiGLU form.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library; the product
+ * path (the HIP library and its Python binding) never does, and the two
+ * share no code, header, table or constant.
+ *
+ * What is computed, and where it comes from:
+ *   - "Tile Kernels" (PyPI project page, v2.0.0), Features: per-token FP8/FP4
+ *     casting of activations, with fused SwiGLU + quantization.
+ *   - "TileKernels" (aiwiki.ai), section Quantization: scale-factor groups of
+ *     16, 32, 64 or 128 channels, optional power-of-two rounding of the scale
+ *     factors, optional packed UE8M0 scale factors; inputs are BF16
+ *     activations.
+ *   - "TileKernels, TileLang kernels for MoE routing and low-precision
+ *     quantization" (hysenlabs.com), section "Seven kernel families": the
+ *     activation function and the narrowing happen in one pass.
+ * The pages print no formula.  The one this oracle follows is the method's
+ * fixed definition, step by step, for every row r and every group j of G
+ * consecutive channels (columns jG .. jG+G-1):
+ *   1. a = max |x_i| over the group, x_i widened exactly from bf16 to fp32;
+ *   2. a = max(a, 1e-4f);
+ *   3. s = a / D in fp32 (IEEE division), D = 448 for e4m3, 6 for e2m1;
+ *   4. optionally s = 2^ceil(log2 s), read exactly from s's exponent and
+ *      mantissa bits;
+ *   5. the scale is stored as fp32 s, or as the UE8M0 byte (biased exponent
+ *      of s) packed four to a little-endian int32 (group 4k+b in byte b);
+ *   6. v_i = x_i / s in fp32 (IEEE division), clamped to [-D, D], then
+ *      rounded to the nearest e4m3 / e2m1 value with ties to the even
+ *      code, keeping the sign (also of zero);
+ *   7. SwiGLU form: x_i is replaced by h_i = fl32(silu32(g_i) * u_i), where
+ *      silu32(g) is the fp32 value nearest to g / (1 + e^-g).
+ * Every float operation below is one IEEE binary32 operation rounded to
+ * nearest-even; build with -O2 -ffp-contract=off and without fast-math.
+ * Results for NaN or Inf inputs are outside the contract.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+enum { ORACLE_E4M3 = 0, ORACLE_E2M1 = 1 };
+enum { ORACLE_SCALE_F32 = 0, ORACLE_SCALE_UE8M0_X4 = 1 };
+
+static float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t bits_from_f32(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* bf16 is the top half of an fp32 bit pattern: widening is exact. */
+static float bf16_to_f32(uint16_t b) { return f32_from_bits((uint32_t)b << 16); }
+
+/* ---- the two target formats, decoded from their definitions ---------- */
+
+/* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent
+ * field 0 is subnormal (m * 2^-9); S.1111.111 is NaN, so the largest finite
+ * magnitude is code 0x7E = 1.75 * 2^8 = 448.  Positive codes 0..126 are
+ * strictly increasing in value. */
+#define E4M3_NCODES 127
+static double e4m3_value(int code)
+{
+    int e = (code >> 3) & 15, m = code & 7;
+    if (e == 0) return ldexp((double)m, -9);
+    return ldexp(1.0 + m / 8.0, e - 7);
+}
+
+/* FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit, no Inf/NaN.
+ * Magnitudes of codes 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+#define E2M1_NCODES 8
+static double e2m1_value(int code)
+{
+    int e = (code >> 1) & 3, m = code & 1;
+    if (e == 0) return 0.5 * m;
+    return ldexp(1.0 + m / 2.0, e - 1);
+}
+
+static double g_e4m3[E4M3_NCODES], g_e2m1[E2M1_NCODES];
+
+/* Filled once when the library is loaded, before any caller thread runs. */
+__attribute__((constructor)) static void init_tables(void)
+{
+    for (int c = 0; c < E4M3_NCODES; ++c) g_e4m3[c] = e4m3_value(c);
+    for (int c = 0; c < E2M1_NCODES; ++c) g_e2m1[c] = e2m1_value(c);
+}
+
+/* Nearest code to a (0 <= a <= largest grid value), ties to the even code.
+ * The grid is ascending and a code's low bit is its mantissa's low bit, so
+ * "even code" is "even mantissa".  a is an fp32 value and every grid value
+ * and midpoint is a short dyadic rational, so all comparisons in double are
+ * exact. */
+static int nearest_code(double a, const double *grid, int n)
+{
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {                       /* smallest k with grid[k] >= a */
+        int mid = (lo + hi) / 2;
+        if (grid[mid] >= a) hi = mid; else lo = mid + 1;
+    }
+    int k = lo;
+    if (k == 0 || grid[k] == a) return k;
+    double midpoint = 0.5 * (grid[k - 1] + grid[k]);
+    if (a < midpoint) return k - 1;
+    if (a > midpoint) return k;
+    return (k % 2 == 0) ? k : k - 1;
+}
+
+/* Step 6 after the division: saturate to [-M, M], round to nearest even,
+ * keep the sign bit of v (so -0.0 and negative values that round to zero
+ * give the negative-zero code). */
+uint8_t oracle_encode_e4m3(float v)
+{
+    const float M = 448.0f;
+    int neg = signbit(v) != 0;
+    float a = fabsf(v);
+    if (a > M) a = M;
+    int code = nearest_code((double)a, g_e4m3, E4M3_NCODES);
+    return (uint8_t)(code | (neg ? 0x80 : 0));
+}
+
+/* Returns one e2m1 nibble (0..15) in the low bits. */
+uint8_t oracle_encode_e2m1(float v)
+{
+    const float M = 6.0f;
+    int neg = signbit(v) != 0;
+    float a = fabsf(v);
+    if (a > M) a = M;
+    int code = nearest_code((double)a, g_e2m1, E2M1_NCODES);
+    return (uint8_t)(code | (neg ? 0x8 : 0));
+}
+
+/* Steps 2-4: the group scale from the group amax.  On return *e8 holds the
+ * biased exponent byte of the result (its UE8M0 encoding when the result
+ * is a power of two). */
+float oracle_group_scale(float amax, int32_t qdtype, int32_t round_pow2, uint8_t *e8)
+{
+    const float D = (qdtype == ORACLE_E4M3) ? 448.0f : 6.0f;
+    const float floor_value = 1e-4f;
+    float a = amax;
+    if (a < floor_value) a = floor_value;
+    float s = a / D;
+    uint32_t b = bits_from_f32(s);
+    uint32_t E = (b >> 23) & 0xFF, m = b & 0x7FFFFF;
+    if (round_pow2) {
+        /* s = 2^(E-127) * (1 + m/2^23) is normal here (s >= 1e-4f / 448),
+         * so ceil(log2 s) = E-127 when m == 0 and E-126 otherwise. */
+        if (m != 0) E += 1;
+        s = f32_from_bits(E << 23);
+    }
+    if (e8) *e8 = (uint8_t)E;
+    return s;
+}
+
+/* Step 7: fp32 nearest to g / (1 + e^-g).  The quotient is formed in the
+ * x87 80-bit format (64-bit significand) and rounded once to fp32.  The
+ * tests check the result for every bf16 g against a 60-digit evaluation. */
+float oracle_silu32(float g)
+{
+    long double x = (long double)g;
+    long double r = x / (1.0L + expl(-x));
+    return (float)r;
+}
+
+/* ---- whole-tensor cast ------------------------------------------------ */
+
+static int valid_common(int64_t rows, int64_t cols, int32_t group, int32_t qdtype,
+                        int32_t round_pow2, int32_t scale_fmt)
+{
+    if (rows < 0 || cols <= 0) return 0;
+    if (group != 16 && group != 32 && group != 64 && group != 128) return 0;
+    if (cols % group != 0) return 0;
+    if (qdtype != ORACLE_E4M3 && qdtype != ORACLE_E2M1) return 0;
+    if (scale_fmt != ORACLE_SCALE_F32 && scale_fmt != ORACLE_SCALE_UE8M0_X4) return 0;
+    if (scale_fmt == ORACLE_SCALE_UE8M0_X4 && (!round_pow2 || (cols / group) % 4 != 0)) return 0;
+    return 1;
+}
+
+/* Cast one row of fp32 values v[0..cols) (already widened from bf16, or the
+ * SwiGLU products) into codes qrow and scales srow. */
+static void cast_row(const float *v, int64_t cols, uint8_t *qrow, void *srow, int32_t group,
+                     int32_t qdtype, int32_t round_pow2, int32_t scale_fmt)
+{
+    int64_t ngroups = cols / group;
+    if (qdtype == ORACLE_E2M1) memset(qrow, 0, (size_t)(cols / 2));
+    if (scale_fmt == ORACLE_SCALE_UE8M0_X4) memset(srow, 0, (size_t)(ngroups / 4) * 4);
+    for (int64_t j = 0; j < ngroups; ++j) {
+        const float *x = v + j * group;
+        float amax = 0.0f;                                   /* step 1 */
+        for (int i = 0; i < group; ++i) {
+            float a = fabsf(x[i]);
+            if (a > amax) amax = a;
+        }
+        uint8_t e8 = 0;
+        float s = oracle_group_scale(amax, qdtype, round_pow2, &e8);   /* steps 2-4 */
+        if (scale_fmt == ORACLE_SCALE_F32) {                 /* step 5 */
+            ((float *)srow)[j] = s;
+        } else {
+            uint32_t *dw = (uint32_t *)srow + j / 4;
+            *dw |= (uint32_t)e8 << (8 * (j % 4));
+        }
+        for (int i = 0; i < group; ++i) {                    /* step 6 */
+            float q = x[i] / s;
+            int64_t c = j * group + i;
+            if (qdtype == ORACLE_E4M3) {
+                qrow[c] = oracle_encode_e4m3(q);
+            } else {
+                uint8_t nib = oracle_encode_e2m1(q);
+                qrow[c / 2] |= (uint8_t)((c % 2 == 0) ? nib : (nib << 4));
+            }
+        }
+    }
+}
+
+/* x: bf16 bits [rows, cols], row stride x_ld elements.
+ * q: [rows, cols] bytes (e4m3) or [rows, cols/2] bytes (e2m1), row stride
+ *    q_ld bytes.
+ * scales: fp32 [rows, cols/group] or int32 [rows, cols/group/4], row stride
+ *    s_ld elements of that type.
+ * Returns 0, or -1 when the arguments describe no valid cast. */
+int oracle_per_token_cast(const uint16_t *x, int64_t rows, int64_t cols, int64_t x_ld,
+                          uint8_t *q, int64_t q_ld, void *scales, int64_t s_ld,
+                          int32_t group, int32_t qdtype, int32_t round_pow2, int32_t scale_fmt,
+                          float *work /* cols floats */)
+{
+    if (!valid_common(rows, cols, group, qdtype, round_pow2, scale_fmt)) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) work[c] = bf16_to_f32(x[r * x_ld + c]);
+        void *srow = (scale_fmt == ORACLE_SCALE_F32) ? (void *)((float *)scales + r * s_ld)
+                                                     : (void *)((uint32_t *)scales + r * s_ld);
+        cast_row(work, cols, q + r * q_ld, srow, group, qdtype, round_pow2, scale_fmt);
+    }
+    return 0;
+}
+
+/* gate_up: bf16 bits [rows, 2*cols]; gate = columns [0, cols), up =
+ * columns [cols, 2*cols).  Outputs as in oracle_per_token_cast with cols. */
+int oracle_swiglu_per_token_cast(const uint16_t *gate_up, int64_t rows, int64_t cols, int64_t x_ld,
+                                 uint8_t *q, int64_t q_ld, void *scales, int64_t s_ld,
+                                 int32_t group, int32_t qdtype, int32_t round_pow2,
+                                 int32_t scale_fmt, float *work /* cols floats */)
+{
+    if (!valid_common(rows, cols, group, qdtype, round_pow2, scale_fmt)) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t *row = gate_up + r * x_ld;
+        for (int64_t c = 0; c < cols; ++c) {
+            float g = bf16_to_f32(row[c]);
+            float u = bf16_to_f32(row[cols + c]);
+            float sg = oracle_silu32(g);
+            work[c] = sg * u;
+        }
+        void *srow = (scale_fmt == ORACLE_SCALE_F32) ? (void *)((float *)scales + r * s_ld)
+                                                     : (void *)((uint32_t *)scales + r * s_ld);
+        cast_row(work, cols, q + r * q_ld, srow, group, qdtype, round_pow2, scale_fmt);
+    }
+    return 0;
+}
+
+/* ---- array forms of the single steps, for the pin tests -------------- */
+
+void oracle_encode_e4m3_n(const float *v, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_encode_e4m3(v[i]);
+}
+
+void oracle_encode_e2m1_n(const float *v, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_encode_e2m1(v[i]);
+}
+
+void oracle_silu32_n(const float *g, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_silu32(g[i]);
+}
+
+void oracle_group_scale_n(const float *amax, float *s, uint8_t *e8, int64_t n, int32_t qdtype,
+                          int32_t round_pow2)
+{
+    for (int64_t i = 0; i < n; ++i) s[i] = oracle_group_scale(amax[i], qdtype, round_pow2, &e8[i]);
+}
+
+/* Step 6's division, elementwise: out[i] = x[i] / s[i]. */
+void oracle_div_n(const float *x, const float *s, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = x[i] / s[i];
+}

@@ -1,0 +1,139 @@
+"""Independent reference for pinning the oracle: the cast composed from library
+routines, vectorised, sharing nothing with ``oracle/``.
+
+Each step of the method is mapped onto a routine whose behaviour is fixed by its
+own documentation rather than by this project:
+  * |x| max over a group          -> numpy ``abs`` + ``max`` (exact);
+  * scale = a / D, v = x / s      -> numpy float32 division (IEEE, nearest-even);
+  * 2^ceil(log2 s)                -> numpy ``frexp`` / ``ldexp`` (exact);
+  * UE8M0 byte of a power of two  -> torch ``float8_e8m0fnu`` cast;
+  * saturating RNE to e4m3        -> numpy ``clip`` then torch ``float8_e4m3fn``
+                                     cast (nearest-even, keeps the sign of zero;
+                                     it does not saturate by itself, hence clip);
+  * RNE to e2m1                   -> numpy ``round`` (half to even) on the
+                                     binade's quantum 0.5 / 1 / 2;
+  * silu32(g)                     -> ``decimal`` exp at 60 digits, then exact
+                                     rounding to binary32 (tests/exact.py).
+"""
+from __future__ import annotations
+
+import decimal
+import functools
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from exact import round_to_f32
+
+D_OF = {"e4m3": np.float32(448.0), "e2m1": np.float32(6.0)}
+FLOOR = np.float32(1e-4)
+
+
+def widen(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def pow2_ceil(s: np.ndarray) -> np.ndarray:
+    m, e = np.frexp(s.astype(np.float32))         # s = m * 2^e, m in [0.5, 1)
+    c = np.where(m == np.float32(0.5), e - 1, e)  # ceil(log2 s)
+    return np.ldexp(np.float32(1.0), c).astype(np.float32)
+
+
+def ue8m0_bytes(s_pow2: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(s_pow2, dtype=np.float32))
+    return t.to(torch.float8_e8m0fnu).view(torch.uint8).numpy()
+
+
+def e4m3_codes(v: np.ndarray) -> np.ndarray:
+    c = np.clip(v.astype(np.float32), np.float32(-448.0), np.float32(448.0))
+    return torch.from_numpy(np.ascontiguousarray(c)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e2m1_codes(v: np.ndarray) -> np.ndarray:
+    v = v.astype(np.float32)
+    a = np.minimum(np.abs(v), np.float32(6.0))
+    q = np.where(a < 2, np.float32(0.5), np.where(a < 4, np.float32(1.0), np.float32(2.0)))
+    val = (np.round(a / q) * q).astype(np.float32)
+    # value -> code from the format's fields: below 1 the subnormal code is
+    # 2*val; from 1 up, code = (exponent+1) << 1 | mantissa bit.
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(val >= 1, val, 1))).astype(np.int32)
+    mbit = (val / np.ldexp(np.float32(1), e) - 1 == 0.5).astype(np.uint8)
+    code = np.where(val < 1, (2 * val).astype(np.uint8), (((e + 1) << 1) | mbit).astype(np.uint8))
+    return (code | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+@functools.lru_cache(maxsize=1)
+def silu32_table() -> np.ndarray:
+    """fp32 nearest to g / (1 + e^-g) for every bf16 bit pattern g (NaN for
+    non-finite g), by 60-digit decimal arithmetic and exact rounding."""
+    ctx = decimal.Context(prec=60, Emax=10**6, Emin=-10**6)
+    out = np.full(65536, np.nan, dtype=np.float32)
+    for b in range(65536):
+        if (b & 0x7F80) == 0x7F80:
+            continue                       # Inf / NaN
+        g = float(widen(np.array([b], dtype=np.uint16))[0])
+        if g >= 1000.0:
+            # g/(1+e^-g) = g*(1 - t), t < e^-1000: rounds to g itself.
+            out[b] = g
+            continue
+        if g <= -1000.0:
+            # |g| e^g/(1+e^g) < 4e38 * e^-1000 << 2^-150: rounds to -0.
+            out[b] = -0.0
+            continue
+        dg = decimal.Decimal(g)
+        val = ctx.divide(dg, ctx.add(decimal.Decimal(1), ctx.exp(-dg)))
+        out[b] = round_to_f32(Fraction(val), negative_zero=(g < 0 or (g == 0 and b == 0x8000)))
+    return out
+
+
+def swiglu_h(gate_up_bits: np.ndarray) -> np.ndarray:
+    rows, c2 = gate_up_bits.shape
+    cols = c2 // 2
+    sg = silu32_table()[gate_up_bits[:, :cols].astype(np.int64)]
+    u = widen(gate_up_bits[:, cols:])
+    return (sg * u).astype(np.float32)
+
+
+def cast_values(x: np.ndarray, group: int, out_dtype: str, round_pow2: bool, scale_fmt: str):
+    """Cast fp32 values x [rows, cols] -> (codes, scales) in the oracle's layout."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    ng = cols // group
+    xg = x.reshape(rows, ng, group)
+    amax = np.abs(xg).max(axis=2) if rows else np.zeros((0, ng), np.float32)
+    a = np.maximum(amax, FLOOR)
+    s = (a / D_OF[out_dtype]).astype(np.float32)
+    if round_pow2:
+        s = pow2_ceil(s)
+    v = (xg / s[:, :, None]).astype(np.float32).reshape(rows, cols)
+    if out_dtype == "e4m3":
+        q = e4m3_codes(v)
+    else:
+        n = e2m1_codes(v)
+        q = (n[:, 0::2] | (n[:, 1::2] << 4)).astype(np.uint8)
+    if scale_fmt == "f32":
+        scales = s
+    else:
+        scales = np.ascontiguousarray(ue8m0_bytes(s)).view(np.int32).reshape(rows, ng // 4)
+    return q, scales
+
+
+def per_token_cast(x_bits, group=128, out_dtype="e4m3", round_pow2=False, scale_fmt="f32"):
+    return cast_values(widen(x_bits), group, out_dtype, round_pow2, scale_fmt)
+
+
+def swiglu_per_token_cast(gate_up_bits, group=128, out_dtype="e4m3", round_pow2=False,
+                          scale_fmt="f32"):
+    return cast_values(swiglu_h(gate_up_bits), group, out_dtype, round_pow2, scale_fmt)
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float32).numpy()
+
+
+def decode_e2m1_nibbles(n: np.ndarray) -> np.ndarray:
+    mag = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float32)[n & 7]
+    return np.where(n & 8, -mag, mag).astype(np.float32)

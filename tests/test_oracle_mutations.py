@@ -1,0 +1,86 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case copies ``oracle/tk_oracle.c``, makes one plausible mistake in the copy
+(a dropped term, a wrong sign or index, a swapped operand, a cheaper but inexact
+operation), builds it, points the ``oracle`` module at that build and runs the
+pin checks from test_oracle_pins.py.  At least one pin must fail; the real
+source is never modified.
+"""
+from __future__ import annotations
+
+import pathlib
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = pathlib.Path(oracle.__file__).resolve().parent / "tk_oracle.c"
+
+# (name, original text, replacement, occurrence index or None for all)
+MUTATIONS = [
+    ("ties away from the even code", "return (k % 2 == 0) ? k : k - 1;", "return k;", None),
+    ("ties toward zero", "return (k % 2 == 0) ? k : k - 1;", "return k - 1;", None),
+    ("e4m3 saturates at 240", "const float M = 448.0f;", "const float M = 240.0f;", None),
+    ("scale by reciprocal multiply", "float s = a / D;", "float s = a * (1.0f / D);", None),
+    ("x/s by reciprocal multiply", "float q = x[i] / s;", "float q = x[i] * (1.0f / s);", None),
+    ("pow2 rounds down", "if (m != 0) E += 1;", "(void)m;", None),
+    ("pow2 always bumps", "if (m != 0) E += 1;", "E += 1; (void)m;", None),
+    ("no amax floor", "if (a < floor_value) a = floor_value;", "(void)floor_value;", None),
+    ("floor 1e-3", "const float floor_value = 1e-4f;", "const float floor_value = 1e-3f;", None),
+    ("amax without abs", "float a = fabsf(x[i]);", "float a = x[i];", None),
+    ("sign of zero dropped", "int neg = signbit(v) != 0;", "int neg = v < 0;", 0),
+    ("e2m1 nibbles swapped", "(c % 2 == 0) ? nib : (nib << 4)", "(c % 2 == 1) ? nib : (nib << 4)", None),
+    ("UE8M0 big-endian", "<< (8 * (j % 4))", "<< (8 * (3 - j % 4))", None),
+    ("e4m3 subnormal step 2^-10", "ldexp((double)m, -9)", "ldexp((double)m, -10)", None),
+    ("e4m3 bias 8", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)", None),
+    ("e2m1 bias 2", "ldexp(1.0 + m / 2.0, e - 1)", "ldexp(1.0 + m / 2.0, e - 2)", None),
+    ("silu sign flipped", "x / (1.0L + expl(-x))", "x / (1.0L + expl(x))", None),
+    ("silu in fp32 with expf", "long double r = x / (1.0L + expl(-x));",
+     "float r = (float)x / (1.0f + expf(-(float)x));", None),
+    ("gate and up swapped", "float g = bf16_to_f32(row[c]);\n            float u = bf16_to_f32(row[cols + c]);",
+     "float u = bf16_to_f32(row[c]);\n            float g = bf16_to_f32(row[cols + c]);", None),
+    ("group offset off by one group", "const float *x = v + j * group;",
+     "const float *x = v + ((j + 1) % ngroups) * group;", None),
+]
+
+
+def _checks():
+    gold = pins._golden()
+    out = [lambda c=c: pins.test_hand_examples(c) for c in gold["cases"]]
+    out += [pins.test_e4m3_tie_table, pins.test_e2m1_tie_table, pins.test_floor_constant_bits,
+            pins.test_e4m3_exhaustive_bf16_times_pow2_vs_torch,
+            pins.test_e2m1_exhaustive_bf16_times_pow2_vs_quantum_rounding,
+            lambda: pins.test_scale_division_exact_all_bf16_amax("e4m3", 448),
+            lambda: pins.test_scale_division_exact_all_bf16_amax("e2m1", 6),
+            lambda: pins.test_pow2_round_up_exact("e4m3", 448),
+            pins.test_division_vs_exact_and_numpy,
+            lambda: pins.test_whole_tensor_division_hard_cases("e4m3"),
+            pins.test_silu32_every_bf16_gate_vs_60_digit_decimal,
+            pins.test_swiglu_sweep_vs_library_composition,
+            lambda: pins.test_whole_tensor_vs_library_composition(32, "e2m1", True, "ue8m0", 3, 4)]
+    return out
+
+
+@pytest.mark.parametrize("name,old,new,occ", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new, occ):
+    text = SRC.read_text()
+    assert old in text, f"mutation anchor not found: {old!r}"
+    if occ is None:
+        mutated = text.replace(old, new)
+    else:
+        parts = text.split(old)
+        mutated = old.join(parts[: occ + 1]) + new + old.join(parts[occ + 1:])
+    assert mutated != text
+    src = tmp_path / "mutant.c"
+    src.write_text(mutated)
+    lib = oracle.compile_source(src, tmp_path / "libmutant.so")
+    caught = None
+    with oracle.using(lib):
+        for check in _checks():
+            try:
+                check()
+            except (AssertionError, ValueError) as e:
+                caught = e
+                break
+    assert caught is not None, f"no pin caught the planted mistake: {name}"

@@ -1,0 +1,386 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test ties one step of the oracle to hand-derived values, a library routine
+with documented semantics, an exact-arithmetic evaluation, or brute force over
+a finite domain:
+  * hand examples and tie tables        -> tests/golden/hand_examples.json
+  * e4m3 rounding                       -> torch's float8_e4m3fn cast (after clip)
+  * e2m1 rounding                       -> numpy half-to-even on the binade quantum
+  * scale division and the x/s division -> exact rationals, numpy float32 division
+  * power-of-two round-up, UE8M0 byte   -> exact integer ceil(log2), torch e8m0
+  * silu32                              -> 60-digit decimal, every bf16 gate
+  * whole tensors (layout, packing)     -> tests/libref.py (library composition)
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import random
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import libref
+from exact import ceil_log2, f32_bits, f32_from_bits, round_to_f32
+from activation_quantization_token_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+FINITE_BF16 = np.array([b for b in range(65536) if (b & 0x7F80) != 0x7F80], dtype=np.uint16)
+NONNEG_BF16 = FINITE_BF16[FINITE_BF16 < 0x8000]
+
+
+def widen(bits):
+    return libref.widen(bits)
+
+
+# ---------------------------------------------------------------- hand examples
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _golden()["cases"], ids=lambda c: c["name"])
+def test_hand_examples(case):
+    reps = case.get("x_repeat_groups", 1)
+    x = np.array(case["x"] * reps, dtype=np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(widen(bits), x), "hand example inputs must be exact bf16"
+    q, s = oracle.per_token_cast(bits.reshape(1, -1), case["group"], case["out_dtype"],
+                                 case["round_pow2"], case["scale_fmt"])
+    if "codes" in case:
+        want = np.array([int(c, 16) for c in case["codes"]] * reps, dtype=np.uint8)
+        assert q.reshape(-1).tolist() == want.tolist()
+    if "packed_codes" in case:
+        want = np.array([int(c, 16) for c in case["packed_codes"]] * reps, dtype=np.uint8)
+        assert q.reshape(-1).tolist() == want.tolist()
+    if "scale_f32_bits" in case:
+        assert s.shape == (1, reps)
+        assert [f32_bits(float(v)) for v in s.reshape(-1)] == [int(case["scale_f32_bits"], 16)] * reps
+    if "ue8m0_bytes" in case:
+        assert s.dtype == np.int32
+        assert list(s.reshape(-1).view(np.uint8)) == case["ue8m0_bytes"]
+        b = case["ue8m0_bytes"]
+        assert int(s.reshape(-1)[0]) & 0xFFFFFFFF == b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24
+
+
+def test_e4m3_tie_table():
+    cases = _golden()["e4m3_ties"]["cases"]
+    v = np.array([c[0] for c in cases], dtype=np.float32)
+    got = oracle.encode_e4m3(v)
+    assert [f"0x{g:02X}" for g in got] == [c[1] for c in cases]
+
+
+def test_e2m1_tie_table():
+    cases = _golden()["e2m1_ties"]["cases"]
+    v = np.array([c[0] for c in cases], dtype=np.float32)
+    assert oracle.encode_e2m1(v).tolist() == [c[1] for c in cases]
+
+
+def test_floor_constant_bits():
+    # 1e-4 rounded to fp32 is 0x38D1B717; amax below it behaves as amax = floor.
+    assert f32_bits(float(np.float32(1e-4))) == 0x38D1B717
+    fl = np.float32(1e-4)
+    below = np.array([0.0, 1e-30, np.nextafter(fl, np.float32(0)), fl], dtype=np.float32)
+    for dt in ("e4m3", "e2m1"):
+        for p2 in (False, True):
+            s, _ = oracle.group_scale(below, dt, p2)
+            assert len(set(f32_bits(float(v)) for v in s)) == 1
+            above, _ = oracle.group_scale(np.array([np.nextafter(fl, np.float32(1)), 4 * fl]), dt, p2)
+            assert above[0] >= s[0] and above[1] > s[0]
+
+
+# ---------------------------------------------------------------- e4m3 rounding
+
+def _scaled_all_bf16(kmin=-40, kmax=40):
+    """Every finite bf16 value times 2^-k (exact in fp32) for k in [kmin, kmax]."""
+    x = widen(FINITE_BF16).astype(np.float64)
+    ks = np.arange(kmin, kmax + 1, dtype=np.float64)
+    v = x[None, :] * np.exp2(-ks)[:, None]
+    v = v[np.abs(v) < 2.0**127].astype(np.float32)   # beyond that, x/s never occurs
+    return v.reshape(-1)
+
+
+def test_e4m3_exhaustive_bf16_times_pow2_vs_torch():
+    v = _scaled_all_bf16()
+    got = oracle.encode_e4m3(v)
+    want = libref.e4m3_codes(v)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, first v={v[bad[0]]!r} got {got[bad[0]]:#x} want {want[bad[0]]:#x}"
+
+
+def test_e4m3_random_fp32_vs_torch():
+    rng = np.random.Generator(np.random.PCG64(123))
+    b = rng.integers(0, 2**32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    b = b[(b & 0x7F800000) != 0x7F800000]
+    v = b.view(np.float32)
+    # include the neighbourhood of every grid midpoint
+    grid = libref.decode_e4m3(np.arange(0, 127, dtype=np.uint8)).astype(np.float64)
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    v = np.concatenate([v, near, -near])
+    assert np.array_equal(oracle.encode_e4m3(v), libref.e4m3_codes(v))
+
+
+# ---------------------------------------------------------------- e2m1 rounding
+
+def test_e2m1_exhaustive_bf16_times_pow2_vs_quantum_rounding():
+    v = _scaled_all_bf16()
+    got = oracle.encode_e2m1(v)
+    want = libref.e2m1_codes(v)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, first v={v[bad[0]]!r}"
+
+
+def test_e2m1_neighbours_of_thresholds():
+    grid = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    for i in range(7):
+        m = np.float32((grid[i] + grid[i + 1]) / 2)
+        lo, hi = np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(10))
+        got = oracle.encode_e2m1(np.array([lo, hi, -lo, -hi], dtype=np.float32)).tolist()
+        assert got == [i, i + 1, 8 | i, 8 | (i + 1)]
+
+
+# ---------------------------------------------------------------- scale
+
+@pytest.mark.parametrize("dt,D", [("e4m3", 448), ("e2m1", 6)])
+def test_scale_division_exact_all_bf16_amax(dt, D):
+    a = widen(NONNEG_BF16)
+    s, e8 = oracle.group_scale(a, dt, False)
+    floor = Fraction(float(np.float32(1e-4)))
+    want = [round_to_f32(max(Fraction(float(ai)), floor) / D) for ai in a]
+    assert [f32_bits(float(x)) for x in s] == [f32_bits(w) for w in want]
+    # numpy's float32 division agrees (an independent IEEE implementation)
+    assert np.array_equal(s, (np.maximum(a, np.float32(1e-4)) / np.float32(D)).astype(np.float32))
+    assert np.array_equal(e8, ((s.view(np.uint32) >> 23) & 0xFF).astype(np.uint8))
+
+
+@pytest.mark.parametrize("dt,D", [("e4m3", 448), ("e2m1", 6)])
+def test_pow2_round_up_exact(dt, D):
+    rng = np.random.Generator(np.random.PCG64(7))
+    rnd = rng.integers(0x30000000, 0x7F000000, size=20000, dtype=np.uint32).view(np.float32)
+    a = np.concatenate([widen(NONNEG_BF16), rnd]).astype(np.float32)
+    s, e8 = oracle.group_scale(a, dt, True)
+    plain, _ = oracle.group_scale(a, dt, False)
+    for i in range(a.size):
+        e = ceil_log2(Fraction(float(plain[i])))
+        assert float(s[i]) == 2.0 ** e, (a[i], s[i], e)
+        assert int(e8[i]) == e + 127
+    # torch's e8m0 cast of the exact power of two gives the same byte
+    assert np.array_equal(libref.ue8m0_bytes(s), e8)
+    bf = e8[: NONNEG_BF16.size]
+    lo, hi = (105, 247) if dt == "e4m3" else (112, 253)
+    assert bf.min() == lo and bf.max() == hi
+
+
+# ---------------------------------------------------------------- x / s
+
+def test_division_vs_exact_and_numpy():
+    """v = x / s for the scales the cast produces, s = fl32(max(a,1e-4)/D) with
+    a a bf16 amax, and every bf16 x with |x| <= a (the values that share a
+    group with that amax)."""
+    rng = random.Random(11)
+    x = widen(FINITE_BF16)
+    amax = widen(np.array(rng.sample(list(NONNEG_BF16), 24), dtype=np.uint16))
+    pairs = []
+    for dt in ("e4m3", "e2m1"):
+        s, _ = oracle.group_scale(amax, dt, False)
+        for a, si in zip(amax, s):
+            xs = x[np.abs(x) <= a]
+            if xs.size == 0:
+                continue
+            got = oracle.divide(xs, np.float32(si))
+            want = (xs / np.float32(si)).astype(np.float32)
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+            pairs.append((xs, si))
+    for _ in range(3000):
+        xs, si = pairs[rng.randrange(len(pairs))]
+        xi = float(xs[rng.randrange(xs.size)])
+        got = float(oracle.divide(np.array([xi], np.float32), np.float32(si))[0])
+        want = round_to_f32(Fraction(xi) / Fraction(float(si)), negative_zero=math.copysign(1, xi) < 0)
+        assert f32_bits(got) == f32_bits(want), (xi, si)
+
+
+# ---------------------------------------------------------------- silu32
+
+def test_silu32_every_bf16_gate_vs_60_digit_decimal():
+    table = libref.silu32_table()
+    g = widen(FINITE_BF16)
+    got = oracle.silu32(g)
+    want = table[FINITE_BF16.astype(np.int64)]
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, f"{bad.size} gates differ, first g={g[bad[0]]!r} got {got[bad[0]]!r} want {want[bad[0]]!r}"
+
+
+def test_silu32_closed_forms():
+    # silu(0) = 0 with the sign kept; silu(g) -> g for large g; -> -0 for very negative g;
+    # silu(g) = g/2 exactly in fp32 for tiny |g| (the g^2/4 term is below half an ulp).
+    g = np.array([0.0, -0.0, 2.0**-30, -(2.0**-30), 1e4, -1e4], dtype=np.float32)
+    got = oracle.silu32(g)
+    assert [f32_bits(float(v)) for v in got] == [f32_bits(v) for v in (0.0, -0.0, 2.0**-31, -(2.0**-31), 1e4, -0.0)]
+
+
+# ---------------------------------------------------------------- whole tensors
+
+SWEEP = [(g, dt, p2, sf)
+         for g in (16, 32, 64, 128)
+         for dt in ("e4m3", "e2m1")
+         for p2 in (False, True)
+         for sf in ("f32", "ue8m0")
+         if not (sf == "ue8m0" and not p2)]
+
+
+@pytest.mark.parametrize("group,dt,p2,sf", SWEEP)
+@pytest.mark.parametrize("rows,cols_groups", [(1, 1), (3, 4), (7, 12), (5, 56)])
+def test_whole_tensor_vs_library_composition(group, dt, p2, sf, rows, cols_groups):
+    cols = group * cols_groups
+    if sf == "ue8m0" and cols_groups % 4:
+        pytest.skip("UE8M0 x4 packing needs a multiple of 4 groups per row")
+    x = inputs.generate_small(rows * 1000 + cols, rows, cols, "student_t3" if rows % 2 else "normal")
+    got_q, got_s = oracle.per_token_cast(x, group, dt, p2, sf)
+    want_q, want_s = libref.per_token_cast(x, group, dt, p2, sf)
+    assert np.array_equal(got_q, want_q)
+    assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32))
+
+
+def _division_hard_groups(dt: str, n_amax: int = 300, per_amax: int = 15, seed: int = 17):
+    """Groups of 16 bf16 values [a, x1..x15] in which x/s and x*(1/s) (s from a)
+    round to different codes: the cases that tell a true division from a
+    reciprocal multiply.  Found by numpy + torch alone."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    D = np.float32(448.0 if dt == "e4m3" else 6.0)
+    x_all = widen(FINITE_BF16)
+    pos = NONNEG_BF16[(NONNEG_BF16 >= 0x3000) & (NONNEG_BF16 < 0x6000)]
+    rows = []
+    enc = libref.e4m3_codes if dt == "e4m3" else libref.e2m1_codes
+    for a_bits in rng.choice(pos, n_amax, replace=False):
+        a = widen(np.array([a_bits], dtype=np.uint16))[0]
+        s = np.float32(a / D)
+        sel = np.abs(x_all) <= a
+        xb, xs = FINITE_BF16[sel], x_all[sel]
+        diff = enc((xs / s).astype(np.float32)) != enc((xs * (np.float32(1) / s)).astype(np.float32))
+        hits = xb[diff][:per_amax]
+        if hits.size:
+            row = np.zeros(16, dtype=np.uint16)
+            row[0] = a_bits
+            row[1:1 + hits.size] = hits
+            rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("dt", ["e4m3", "e2m1"])
+def test_whole_tensor_division_hard_cases(dt):
+    x = _division_hard_groups(dt)
+    assert x.shape[0] > 20, "the search should find division-sensitive groups"
+    q, s = oracle.per_token_cast(x, 16, dt, False, "f32")
+    q2, s2 = libref.per_token_cast(x, 16, dt, False, "f32")
+    assert np.array_equal(s.view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(q, q2)
+
+
+@pytest.mark.parametrize("w", inputs.WORKLOADS, ids=lambda w: f"workload{w.index}")
+def test_workload_rows_vs_library_composition(w):
+    x = inputs.generate(w, rows=48)
+    fn_o = oracle.swiglu_per_token_cast if w.swiglu else oracle.per_token_cast
+    fn_l = libref.swiglu_per_token_cast if w.swiglu else libref.per_token_cast
+    q, s = fn_o(x, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)
+    q2, s2 = fn_l(x, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)
+    assert np.array_equal(q, q2)
+    assert np.array_equal(s.view(np.uint32), s2.view(np.uint32))
+
+
+def test_swiglu_sweep_vs_library_composition():
+    rng = np.random.Generator(np.random.PCG64(5))
+    # every bf16 gate pattern appears: gates are a permutation of the finite bf16 set
+    gates = rng.permutation(FINITE_BF16)[: 64 * 1020].reshape(64, 1020)
+    ups = inputs.generate_small(9, 64, 1024)
+    # keep h finite (non-finite values are outside the cast's contract): next to a
+    # gate beyond 2^100 the up value is 0.5
+    big = np.abs(widen(np.pad(gates, ((0, 0), (0, 4)), constant_values=0x3F80))) > 2.0**100
+    ups[big] = 0x3F00
+    gate_up = np.concatenate([np.pad(gates, ((0, 0), (0, 4)), constant_values=0x3F80), ups], axis=1)
+    for group, dt, p2, sf in [(128, "e4m3", True, "f32"), (32, "e2m1", True, "ue8m0"),
+                              (16, "e4m3", False, "f32"), (64, "e4m3", True, "ue8m0")]:
+        q, s = oracle.swiglu_per_token_cast(gate_up, group, dt, p2, sf)
+        q2, s2 = libref.swiglu_per_token_cast(gate_up, group, dt, p2, sf)
+        assert np.array_equal(q, q2)
+        assert np.array_equal(s.view(np.uint32), s2.view(np.uint32))
+
+
+def test_row_stride_is_respected():
+    x = inputs.generate_small(3, 6, 512)
+    wide = np.full((6, 512 + 64), 0x7F7F, dtype=np.uint16)   # garbage beyond cols
+    wide[:, :512] = x
+    a = oracle.per_token_cast(x, 32, "e2m1", True, "ue8m0")
+    b = oracle.per_token_cast(wide[:, :512], 32, "e2m1", True, "ue8m0")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("args", [
+    dict(group=48), dict(group=128, cols=64), dict(scale_fmt="ue8m0", round_pow2=False),
+    dict(scale_fmt="ue8m0", round_pow2=True, group=16, cols=48)])
+def test_invalid_arguments_rejected(args):
+    group = args.get("group", 32)
+    cols = args.get("cols", 256)
+    x = np.zeros((2, cols), dtype=np.uint16)
+    with pytest.raises((ValueError, KeyError, ZeroDivisionError)):
+        oracle.per_token_cast(x, group, "e4m3", args.get("round_pow2", True), args.get("scale_fmt", "f32"))
+
+
+# ---------------------------------------------------------------- invariants
+
+def _decode(q, dt, cols):
+    if dt == "e4m3":
+        return libref.decode_e4m3(q)
+    n = np.empty((q.shape[0], cols), dtype=np.uint8)
+    n[:, 0::2] = q & 0xF
+    n[:, 1::2] = q >> 4
+    return libref.decode_e2m1_nibbles(n)
+
+
+@pytest.mark.parametrize("w", inputs.WORKLOADS, ids=lambda w: f"workload{w.index}")
+def test_invariants(w):
+    rows = w.rows if w.index == 0 else 64
+    x = inputs.generate(w, rows=rows)
+    if w.swiglu:
+        q, s = oracle.swiglu_per_token_cast(x, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)
+        xv = libref.swiglu_h(x)
+    else:
+        q, s = oracle.per_token_cast(x, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)
+        xv = widen(x)
+    D = 448.0 if w.out_dtype == "e4m3" else 6.0
+    ng = w.cols // w.group
+    if w.scale_fmt == "f32":
+        sc = s.astype(np.float64)
+    else:
+        e8 = s.view(np.uint8).reshape(rows, ng).astype(np.int64)
+        lo, hi = (105, 247) if w.out_dtype == "e4m3" else (112, 253)
+        assert e8.min() >= lo and e8.max() <= hi
+        sc = np.exp2(e8 - 127.0)
+    dq = _decode(q, w.out_dtype, w.cols).astype(np.float64)
+    assert np.abs(dq).max() <= D
+    xg = xv.astype(np.float64).reshape(rows, ng, w.group)
+    amax = np.maximum(np.abs(xg).max(axis=2), float(np.float32(1e-4)))
+    if w.round_pow2:
+        assert np.all(sc * D >= amax * (1 - 2**-23)) and np.all(sc * D < 2 * amax * (1 + 2**-22))
+        assert np.all(np.log2(sc) == np.round(np.log2(sc)))
+    # sign is kept (including on codes that round to zero)
+    sb = 0x80 if w.out_dtype == "e4m3" else None
+    if sb is not None:
+        assert np.array_equal((q & 0x80) != 0, np.signbit(xv))
+    # each code is within half an e4m3/e2m1 step of x/s (plus the fp32 rounding of x/s)
+    v = xg / sc[:, :, None]
+    err = np.abs(dq.reshape(rows, ng, w.group) - np.clip(v, -D, D))
+    av = np.minimum(np.abs(v), D)
+    if w.out_dtype == "e4m3":
+        step = np.where(av < 2.0**-6, 2.0**-9, np.exp2(np.floor(np.log2(np.maximum(av, 2.0**-6)))) / 8)
+    else:
+        step = np.where(av < 2, 0.5, np.where(av < 4, 1.0, 2.0))
+    assert np.all(err <= step / 2 * (1 + 1e-5) + 1e-30)
+    if w.zero_last_row:
+        assert not q[-1].any()
