@@ -1,0 +1,23 @@
+"""MI355X (gfx950) per-token / per-group FP8 E4M3 / FP4 E2M1 activation cast.
+
+The product path is the HIP library ``libtk_quant.so`` (C ABI in
+``include/tk_quant.h``) and the thin ctypes binding in ``binding.py``.  Build
+the library with ``python -m activation_quantization_token_amd.build``.
+"""
+from .binding import (  # noqa: F401
+    GROUPS,
+    QDTYPES,
+    SCALE_FMTS,
+    TkError,
+    empty_outputs,
+    load_library,
+    per_token_cast,
+    silu32_bf16,
+    swiglu_per_token_cast,
+    tk_abi_version,
+    tk_per_token_cast,
+    tk_prepare_device,
+    tk_silu32_bf16,
+    tk_status_string,
+    tk_swiglu_per_token_cast,
+)

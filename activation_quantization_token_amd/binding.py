@@ -1,0 +1,182 @@
+"""Thin Python binding over libtk_quant.so (argument marshalling only).
+
+PyTorch supplies device memory and the current stream; every step of the cast
+runs in the library's HIP kernels.  The functions named like the C ABI
+(``tk_per_token_cast`` ...) take tensors that the caller allocated; the
+convenience forms (``per_token_cast`` ...) allocate the outputs.
+
+There is no fallback: if the library is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import threading
+
+import torch  # imported first so the library binds to torch's HIP runtime
+
+_PKG = pathlib.Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libtk_quant.so"
+
+TK_SUCCESS = 0
+QDTYPES = {"e4m3": 0, "e2m1": 1}
+SCALE_FMTS = {"f32": 0, "ue8m0": 1}
+GROUPS = (16, 32, 64, 128)
+
+_lock = threading.Lock()
+_lib_handle = None
+
+
+class TkError(RuntimeError):
+    """A tk_* call returned a status other than TK_SUCCESS."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load_library(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
+    """Load (once) and return the HIP library; raises if it is not built."""
+    global _lib_handle
+    with _lock:
+        if _lib_handle is not None and path is None:
+            return _lib_handle
+        p = pathlib.Path(path) if path is not None else LIB_PATH
+        if not p.exists():
+            raise RuntimeError(
+                f"{p} is not built; run `python -m activation_quantization_token_amd.build`")
+        lib = ctypes.CDLL(str(p))
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        for name in ("tk_per_token_cast", "tk_swiglu_per_token_cast"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, i32, i32, i32, i32, vp]
+            fn.restype = ctypes.c_int
+        lib.tk_silu32_bf16.argtypes = [vp, vp, i64, vp]
+        lib.tk_silu32_bf16.restype = ctypes.c_int
+        lib.tk_prepare_device.argtypes = []
+        lib.tk_prepare_device.restype = ctypes.c_int
+        lib.tk_status_string.argtypes = [i32]
+        lib.tk_status_string.restype = ctypes.c_char_p
+        lib.tk_abi_version.argtypes = []
+        lib.tk_abi_version.restype = ctypes.c_int32
+        if path is None:
+            _lib_handle = lib
+        return lib
+
+
+def tk_status_string(status: int) -> str:
+    return load_library().tk_status_string(int(status)).decode()
+
+
+def tk_abi_version() -> int:
+    return int(load_library().tk_abi_version())
+
+
+def _check(status: int):
+    if status != TK_SUCCESS:
+        raise TkError(status, tk_status_string(status))
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def tk_prepare_device() -> None:
+    _check(load_library().tk_prepare_device())
+
+
+def tk_silu32_bf16(g: int, out: int, n: int, stream: int) -> int:
+    """Raw C call: out[i] = silu32(g[i]) for bf16 gates; returns the tk_status code."""
+    return load_library().tk_silu32_bf16(g, out, n, stream)
+
+
+def silu32_bf16(g: torch.Tensor, stream=None) -> torch.Tensor:
+    """Diagnostic: the fused kernel's silu32 applied to a 1-D bf16 tensor."""
+    if g.dtype != torch.bfloat16 or g.dim() != 1 or not g.is_cuda or g.stride(0) != 1:
+        raise TypeError("g must be a contiguous 1-D torch.bfloat16 GPU tensor")
+    out = torch.empty(g.shape, dtype=torch.float32, device=g.device)
+    _check(tk_silu32_bf16(g.data_ptr(), out.data_ptr(), g.numel(), _stream_handle(stream, g.device)))
+    return out
+
+
+def tk_per_token_cast(x: int, rows: int, cols: int, x_ld: int, q: int, q_ld: int, scales: int,
+                      s_ld: int, group: int, out_dtype: int, round_pow2: int, scale_fmt: int,
+                      stream: int) -> int:
+    """Raw C call with integer pointers; returns the tk_status code."""
+    return load_library().tk_per_token_cast(x, rows, cols, x_ld, q, q_ld, scales, s_ld, group,
+                                            out_dtype, round_pow2, scale_fmt, stream)
+
+
+def tk_swiglu_per_token_cast(gate_up: int, rows: int, cols: int, x_ld: int, q: int, q_ld: int,
+                             scales: int, s_ld: int, group: int, out_dtype: int, round_pow2: int,
+                             scale_fmt: int, stream: int) -> int:
+    """Raw C call with integer pointers; returns the tk_status code."""
+    return load_library().tk_swiglu_per_token_cast(gate_up, rows, cols, x_ld, q, q_ld, scales,
+                                                   s_ld, group, out_dtype, round_pow2, scale_fmt,
+                                                   stream)
+
+
+def _check_input(x: torch.Tensor, what: str):
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError(f"{what} must be a 2-D torch.bfloat16 tensor")
+    if not x.is_cuda:
+        raise TypeError(f"{what} must be on a GPU device")
+    if x.stride(1) != 1:
+        raise ValueError(f"{what} must have contiguous rows (stride(1) == 1)")
+
+
+def empty_outputs(rows: int, cols: int, group: int, out_dtype: str, scale_fmt: str, device):
+    """Allocate (codes, scales) for a cast of `cols` output channels."""
+    q_cols = cols if out_dtype == "e4m3" else cols // 2
+    q = torch.empty((rows, q_cols), dtype=torch.uint8, device=device)
+    if scale_fmt == "f32":
+        s = torch.empty((rows, cols // group), dtype=torch.float32, device=device)
+    else:
+        s = torch.empty((rows, cols // group // 4), dtype=torch.int32, device=device)
+    return q, s
+
+
+def _run(fn, x, cols, group, out_dtype, round_pow2, scale_fmt, out, stream):
+    if group not in GROUPS:
+        raise ValueError(f"group must be one of {GROUPS}")
+    if out_dtype not in QDTYPES or scale_fmt not in SCALE_FMTS:
+        raise ValueError("out_dtype must be 'e4m3'|'e2m1' and scale_fmt 'f32'|'ue8m0'")
+    rows = x.shape[0]
+    if out is None:
+        if cols % group or (scale_fmt == "ue8m0" and (cols // group) % 4):
+            raise ValueError("cols must be a multiple of group (of 4*group for ue8m0 scales)")
+        q, s = empty_outputs(rows, cols, group, out_dtype, scale_fmt, x.device)
+    else:
+        q, s = out
+    for t in (q, s):
+        if t.device != x.device or t.dim() != 2 or t.stride(1) != 1 or t.shape[0] != rows:
+            raise ValueError("outputs must be 2-D, row-contiguous, on the input's device")
+    st = fn(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0), s.data_ptr(),
+            s.stride(0), group, QDTYPES[out_dtype], int(bool(round_pow2)), SCALE_FMTS[scale_fmt],
+            _stream_handle(stream, x.device))
+    _check(st)
+    return q, s
+
+
+def per_token_cast(x: torch.Tensor, group: int = 128, out_dtype: str = "e4m3",
+                   round_pow2: bool = False, scale_fmt: str = "f32", out=None, stream=None):
+    """bf16 x [rows, cols] -> (codes uint8, scales float32 | int32), see include/tk_quant.h."""
+    _check_input(x, "x")
+    return _run(tk_per_token_cast, x, x.shape[1], group, out_dtype, round_pow2, scale_fmt, out,
+                stream)
+
+
+def swiglu_per_token_cast(gate_up: torch.Tensor, group: int = 128, out_dtype: str = "e4m3",
+                          round_pow2: bool = False, scale_fmt: str = "f32", out=None,
+                          stream=None):
+    """bf16 gate_up [rows, 2*I] -> cast of silu(gate) * up, (codes, scales)."""
+    _check_input(gate_up, "gate_up")
+    if gate_up.shape[1] % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    return _run(tk_swiglu_per_token_cast, gate_up, gate_up.shape[1] // 2, group, out_dtype,
+                round_pow2, scale_fmt, out, stream)

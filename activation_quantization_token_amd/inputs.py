@@ -15,8 +15,14 @@ The result is rounded float64 -> float32 -> bf16, both round-to-nearest-even.
 from __future__ import annotations
 
 import dataclasses
+import os
+import pathlib
 
 import numpy as np
+
+RECIPE_VERSION = 1
+CACHE_DIR = pathlib.Path(os.environ.get("TK_INPUT_CACHE",
+                                        pathlib.Path(__file__).resolve().parent.parent / "build" / "inputs"))
 
 
 @dataclasses.dataclass(frozen=True)
@@ -94,14 +100,25 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def generate(w: Workload | int, rows: int | None = None) -> np.ndarray:
+def generate(w: Workload | int, rows: int | None = None, cache: bool = False) -> np.ndarray:
     """bf16 bit patterns [rows, in_cols] for workload ``w``.
 
     ``rows`` (default: the workload's) changes the matrix height; the outlier
-    count and the zero row follow the recipe for that height."""
+    count and the zero row follow the recipe for that height.  With ``cache``
+    the matrix is kept as a .npy file under CACHE_DIR for later calls."""
     if isinstance(w, int):
         w = WORKLOADS[w]
     R = w.rows if rows is None else rows
+    if cache:
+        path = CACHE_DIR / f"w{w.index}_r{R}_v{RECIPE_VERSION}.npy"
+        if path.exists():
+            return np.load(path)
+        x = generate(w, R, cache=False)
+        path.parent.mkdir(parents=True, exist_ok=True)
+        tmp = path.with_suffix(f".tmp{os.getpid()}.npy")
+        np.save(tmp, x)
+        os.replace(tmp, path)
+        return x
     rng = np.random.Generator(np.random.PCG64(w.seed))
     if w.base == "swiglu":
         gate = 2.0 * rng.standard_normal((R, w.cols))

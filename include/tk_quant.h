@@ -1,0 +1,141 @@
+/*
+ * tk_quant.h -- C ABI of the MI355X (gfx950) per-token / per-group activation
+ * cast and its fused SwiGLU form.
+ *
+ * The operation (sources on the pages):
+ *   - "Tile Kernels" (PyPI project page, v2.0.0), Features: per-token FP8 /
+ *     FP4 casting of activations, and fused SwiGLU + quantization.
+ *   - "TileKernels" (aiwiki.ai), section Quantization: the per-token cast takes
+ *     BF16 activations, uses scale-factor groups of 16, 32, 64 or 128 channels,
+ *     and can round scale factors to powers of two and pack them as UE8M0.
+ *   - "TileKernels, TileLang kernels for MoE routing and low-precision
+ *     quantization" (hysenlabs.com), section "Seven kernel families": the
+ *     SwiGLU and the narrowing run in one pass, with no intermediate tensor
+ *     written to memory.
+ * For each row r and each group j of G consecutive channels
+ * (columns jG .. jG+G-1):
+ *     a   = max(max_i |x_i|, 1e-4f)                  (x_i widened from bf16)
+ *     s   = a / D  (IEEE fp32 division; D = 448 for E4M3, 6 for E2M1)
+ *     s   = 2^ceil(log2 s)  if round_pow2            (from s's exponent bits)
+ *     q_i = RNE(clamp(x_i / s, -D, D))               (x_i / s: IEEE fp32)
+ * with round-to-nearest-even onto the target grid, ties to the even code, and
+ * the sign kept also on zero.  The SwiGLU form casts
+ *     h_i = fl32(silu32(gate_i) * up_i),  silu32(g) = fp32 nearest to g/(1+e^-g)
+ * (correctly rounded; the product is one fp32 multiply).  h is never written.
+ *
+ * Formats:
+ *   TK_QDTYPE_E4M3: OCP FP8 E4M3FN, one byte per element, max 448.
+ *   TK_QDTYPE_E2M1: FP4 E2M1, two per byte, element 2i in bits 0..3 and
+ *                   element 2i+1 in bits 4..7; max 6.
+ *   TK_SCALE_F32:      fp32 s per group, [rows, cols/G].
+ *   TK_SCALE_UE8M0_X4: the biased exponent byte of s (s = 2^(byte-127)), four
+ *                      groups per little-endian int32 (group 4k+b in byte b),
+ *                      [rows, cols/G/4] int32.  Requires round_pow2 != 0.
+ *
+ * Ownership and execution: every pointer is a device pointer owned by the
+ * caller.  Calls enqueue work on `stream` (a hipStream_t; NULL = the null
+ * stream) and return without waiting; outputs are valid once the stream
+ * reaches that point.  The library allocates no per-call memory.  All
+ * argument checks run on the host before anything is enqueued: on error
+ * nothing is launched and the outputs are untouched.  Inputs with NaN or Inf
+ * give unspecified codes and scales (outside the contract).
+ */
+#ifndef TK_QUANT_H
+#define TK_QUANT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TK_ABI_VERSION 1
+
+typedef enum tk_status {
+    TK_SUCCESS = 0,
+    TK_ERROR_INVALID_VALUE = 1, /* bad size, group, format or null pointer         */
+    TK_ERROR_UNSUPPORTED = 2,   /* valid request that this build does not provide   */
+    TK_ERROR_MISALIGNED = 3,    /* a pointer or row stride breaks the alignment rule */
+    TK_ERROR_LAUNCH = 4,        /* the HIP runtime refused the launch               */
+    TK_ERROR_DEVICE = 5         /* no usable gfx950 device / runtime error          */
+} tk_status;
+
+typedef enum tk_qdtype { TK_QDTYPE_E4M3 = 0, TK_QDTYPE_E2M1 = 1 } tk_qdtype;
+typedef enum tk_scale_fmt { TK_SCALE_F32 = 0, TK_SCALE_UE8M0_X4 = 1 } tk_scale_fmt;
+
+/*
+ * tk_per_token_cast -- cast bf16 activations to FP8 E4M3 or FP4 E2M1 codes
+ * plus per-(row, group) scales.  ("TileKernels" (aiwiki.ai), Quantization.)
+ *
+ *   x        bf16 [rows, cols], row stride x_ld elements (x_ld >= cols).
+ *   rows     >= 0; rows == 0 returns TK_SUCCESS and launches nothing.
+ *   cols     > 0, a multiple of group (and of 4*group for TK_SCALE_UE8M0_X4).
+ *   q        codes: uint8 [rows, cols] for E4M3 or [rows, cols/2] for E2M1,
+ *            row stride q_ld bytes (q_ld >= cols resp. cols/2).
+ *   scales   float [rows, cols/group] (TK_SCALE_F32) or int32
+ *            [rows, cols/group/4] (TK_SCALE_UE8M0_X4); row stride s_ld
+ *            elements of that type (s_ld >= the row length).
+ *   group    16, 32, 64 or 128.
+ *   out_dtype  TK_QDTYPE_E4M3 or TK_QDTYPE_E2M1.
+ *   round_pow2 nonzero: scales rounded up to a power of two.
+ *   scale_fmt  TK_SCALE_F32 or TK_SCALE_UE8M0_X4 (the latter needs round_pow2).
+ *   stream   hipStream_t as void*.
+ *
+ * Alignment (TK_ERROR_MISALIGNED otherwise): x and 2*x_ld multiples of 16
+ * bytes; q and q_ld multiples of 8 bytes (E4M3) or 4 bytes (E2M1); scales a
+ * multiple of 4 bytes.  Output rows must not overlap the input or each other.
+ */
+tk_status tk_per_token_cast(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
+                            void *q, int64_t q_ld, void *scales, int64_t s_ld,
+                            int32_t group, int32_t out_dtype, int32_t round_pow2,
+                            int32_t scale_fmt, void *stream);
+
+/*
+ * tk_swiglu_per_token_cast -- fused SwiGLU + cast.  ("Tile Kernels" (PyPI,
+ * v2.0.0), Features; "TileKernels, TileLang kernels for MoE routing and
+ * low-precision quantization" (hysenlabs.com), Seven kernel families.)
+ *
+ *   gate_up  bf16 [rows, 2*cols], row stride x_ld elements (x_ld >= 2*cols);
+ *            gate = columns [0, cols), up = columns [cols, 2*cols).
+ *   All other arguments, layouts, alignment rules and errors are those of
+ *   tk_per_token_cast with `cols` output channels; in addition 2*cols must
+ *   keep the up half 16-byte aligned (cols a multiple of 8, which every
+ *   valid group size implies).
+ *
+ * The first call on a device builds the library's correctly rounded silu32
+ * table on that device (a one-time kernel followed by a wait on `stream`);
+ * call tk_prepare_device() beforehand to keep that wait out of a region that
+ * must not synchronise (e.g. graph capture).
+ */
+tk_status tk_swiglu_per_token_cast(const void *gate_up, int64_t rows, int64_t cols, int64_t x_ld,
+                                   void *q, int64_t q_ld, void *scales, int64_t s_ld,
+                                   int32_t group, int32_t out_dtype, int32_t round_pow2,
+                                   int32_t scale_fmt, void *stream);
+
+/*
+ * tk_silu32_bf16 -- diagnostic: out[i] = silu32(g[i]) for n bf16 gates, by the
+ * same device lookup that tk_swiglu_per_token_cast uses for its gate half
+ * (fp32 nearest to g / (1 + e^-g)).  g: bf16 [n] (2-byte aligned), out: fp32
+ * [n] (4-byte aligned), both device pointers; n >= 0.  Asynchronous on
+ * `stream` after the first call on a device (see tk_swiglu_per_token_cast).
+ */
+tk_status tk_silu32_bf16(const void *g, void *out, int64_t n, void *stream);
+
+/*
+ * tk_prepare_device -- build the per-device tables used by the SwiGLU form on
+ * the current HIP device, and wait until they are ready.  Idempotent; safe to
+ * call from several threads.
+ */
+tk_status tk_prepare_device(void);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *tk_status_string(int32_t status);
+
+/* TK_ABI_VERSION of the built library. */
+int32_t tk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TK_QUANT_H */

@@ -1,0 +1,123 @@
+"""The C-ABI library loads, exports every declared entry point, and validates
+arguments on the host (CPU only: nothing here reaches the GPU runtime)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import activation_quantization_token_amd as tk
+from activation_quantization_token_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tk_quant.h")
+
+INVALID, UNSUPPORTED, MISALIGNED = 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("tk_per_token_cast", "tk_swiglu_per_token_cast", "tk_status_string", "tk_abi_version",
+              "tk_prepare_device", "tk_silu32_bf16"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tk.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in tk_quant.h but not exported"
+    # exported with C linkage, i.e. unmangled
+    raw = ctypes.CDLL(str(binding.LIB_PATH))
+    for name in declared_functions():
+        ctypes.cast(getattr(raw, name), ctypes.c_void_p)
+
+
+def test_abi_version_and_status_strings():
+    assert tk.tk_abi_version() == 1
+    assert tk.tk_status_string(0) == "TK_SUCCESS"
+    for st in range(1, 6):
+        assert tk.tk_status_string(st).startswith("TK_ERROR_")
+    assert tk.tk_status_string(99) == "TK_ERROR_UNKNOWN"
+
+
+# Fake, suitably aligned device addresses: validation must reject before any
+# pointer is used, and a successful rows == 0 call must not touch them.
+X, Q, S = 0x10000, 0x20000, 0x30000
+
+
+def call(fn=tk.tk_per_token_cast, x=X, rows=4, cols=256, x_ld=None, q=Q, q_ld=None, s=S, s_ld=None,
+         group=32, out_dtype=0, round_pow2=1, scale_fmt=0, swiglu=False):
+    in_cols = 2 * cols if swiglu else cols
+    x_ld = in_cols if x_ld is None else x_ld
+    q_ld = (cols if out_dtype == 0 else cols // 2) if q_ld is None else q_ld
+    if s_ld is None:
+        g = group if group > 0 else 32
+        s_ld = max(cols // g, 1) if scale_fmt == 0 else max(cols // g // 4, 1)
+    return fn(x, rows, cols, x_ld, q, q_ld, s, s_ld, group, out_dtype, round_pow2, scale_fmt, 0)
+
+
+@pytest.mark.parametrize("fn,swiglu", [(tk.tk_per_token_cast, False), (tk.tk_swiglu_per_token_cast, True)])
+@pytest.mark.parametrize("kw,want", [
+    (dict(group=48), INVALID),
+    (dict(group=0), INVALID),
+    (dict(group=256), INVALID),
+    (dict(cols=200), INVALID),                       # not a multiple of the group
+    (dict(cols=0), INVALID),
+    (dict(cols=-32), INVALID),
+    (dict(rows=-1), INVALID),
+    (dict(out_dtype=2), INVALID),
+    (dict(scale_fmt=2), INVALID),
+    (dict(scale_fmt=1, round_pow2=0), INVALID),      # UE8M0 holds powers of two only
+    (dict(scale_fmt=1, cols=96), INVALID),           # 3 groups: not a multiple of 4
+    (dict(x_ld=100), INVALID),                       # row stride below the row length
+    (dict(q_ld=100), INVALID),
+    (dict(s_ld=1), INVALID),
+    (dict(x=0), INVALID),
+    (dict(q=0), INVALID),
+    (dict(s=0), INVALID),
+    (dict(x=X + 8), MISALIGNED),
+    (dict(q=Q + 4), MISALIGNED),
+    (dict(q=Q + 2, out_dtype=1), MISALIGNED),
+    (dict(s=S + 2), MISALIGNED),
+    (dict(x_ld=260, cols=256), MISALIGNED),          # 520-byte rows: not 16-byte multiples
+    (dict(q_ld=260), MISALIGNED),
+])
+def test_validation_errors(fn, swiglu, kw, want):
+    if swiglu and "x_ld" in kw:
+        kw = dict(kw, x_ld=kw["x_ld"] * 2 if want == INVALID else 2 * 256 + 4)
+    assert call(fn, swiglu=swiglu, **kw) == want
+
+
+@pytest.mark.parametrize("fn,swiglu", [(tk.tk_per_token_cast, False), (tk.tk_swiglu_per_token_cast, True)])
+def test_zero_rows_is_a_no_op(fn, swiglu):
+    # rows == 0 succeeds without touching (null) pointers or the device
+    assert call(fn, rows=0, x=0, q=0, s=0, swiglu=swiglu) == 0
+
+
+def test_silu_diagnostic_validation():
+    assert tk.tk_silu32_bf16(X, Q, -1, 0) == INVALID
+    assert tk.tk_silu32_bf16(X, Q, 0, 0) == 0
+    assert tk.tk_silu32_bf16(0, Q, 5, 0) == INVALID
+    assert tk.tk_silu32_bf16(X + 1, Q, 5, 0) == MISALIGNED
+    assert tk.tk_silu32_bf16(X, Q + 2, 5, 0) == MISALIGNED
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        tk.per_token_cast(x, 32)
+    with pytest.raises(TypeError):
+        tk.per_token_cast(x.float(), 32)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load_library(tmp_path / "libtk_quant.so")
