@@ -66,6 +66,35 @@ constexpr int kSiluEntries = 2 * int(kSiluHi - kSiluLo + 1);   // sign interleav
 
 __device__ float g_silu_table[kSiluEntries];
 
+// Round main + tail (|tail| small against |main|) to the nearest fp32, ties
+// to even, as one rounding of the exact sum.  TwoSum (Knuth) gives s + e ==
+// main + tail exactly; s alone decides unless it sits exactly on a midpoint
+// between two fp32 values, where the sign of e decides.  main is never 0 here.
+__device__ float round_sum_to_f32(double main, double tail)
+{
+    const double s = main + tail;
+    const double bb = s - main;
+    const double e = (main - (s - bb)) + (tail - bb);
+    const float f = float(s);
+    if (e == 0.0) return f;
+    const uint32_t fb = __float_as_uint(f);
+    const float away = __uint_as_float(fb + 1u);     // next fp32 away from zero
+    const float toward = __uint_as_float(fb - 1u);   // next fp32 toward zero
+    const bool e_outward = (e > 0.0) == (f > 0.0f);
+    if (s == 0.5 * (double(f) + double(away))) return e_outward ? away : f;
+    if (s == 0.5 * (double(f) + double(toward))) return e_outward ? f : toward;
+    return f;
+}
+
+// One table entry per thread.
+//   |g| < 2^-6: silu(g) = g/2 + g^2/4 - g^4/48 + g^6/480 - 17 g^8/80640 + ...
+//     g/2 + g^2/4 is exact in fp64 (g has 8 significant bits); the tail is
+//     added by round_sum_to_f32.  Here g/2 + g^2/4 can fall exactly on an fp32
+//     midpoint (e.g. g = -1.125 * 2^-17), where only the tail's sign decides.
+//   |g| >= 2^-6: every exact table value lies at least 4e-5 fp32 ulp away
+//     from a midpoint between two fp32 values (checked at 50 digits, subnormal
+//     results included), while the fp64 evaluation errs by well under 2^-26
+//     fp32 ulp, so one fp64 -> fp32 rounding gives the correctly rounded value.
 __global__ void silu_table_kernel()
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -73,14 +102,19 @@ __global__ void silu_table_kernel()
     const uint32_t mag = kSiluLo + uint32_t(i >> 1);
     const uint32_t bits = (uint32_t(i & 1) << 15) | mag;
     const double g = double(__uint_as_float(bits << 16));
-    double r;
-    if (g >= 0.0) {
-        r = g / (1.0 + exp(-g));
+    float r;
+    if (fabs(g) < 0x1p-6) {
+        const double g2 = g * g;
+        const double head = g * 0.5 + g2 * 0.25;
+        const double tail = g2 * g2 * (-1.0 / 48.0 + g2 * (1.0 / 480.0 - g2 * (17.0 / 80640.0)));
+        r = round_sum_to_f32(head, tail);
+    } else if (g >= 0.0) {
+        r = float(g / (1.0 + exp(-g)));
     } else {
         const double e = exp(g);
-        r = (g * e) / (1.0 + e);
+        r = float((g * e) / (1.0 + e));
     }
-    g_silu_table[i] = float(r);   // one round-to-nearest-even step
+    g_silu_table[i] = r;
 }
 
 // ---------------------------------------------------------------------------

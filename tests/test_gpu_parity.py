@@ -225,9 +225,9 @@ def test_extreme_values(dt):
                          0x3F80, 0xBF80, 0x7F00, 0x0100, 0x8100, 0x4000, 0xC000], dtype=np.uint16)
     rng = np.random.Generator(np.random.PCG64(3))
     rows = np.stack([rng.permutation(specials) for _ in range(256)])
-    x = np.tile(rows, (1, 8))                           # 128 columns
-    x[::7] = 0x8000                                     # whole groups of -0.0
-    x[::11] = 0x0001                                    # whole groups of the smallest subnormal
+    x = np.tile(rows, (1, 32))                          # 512 columns: 4 groups of 128
+    x[::7, :128] = 0x8000                               # whole groups of -0.0
+    x[::11, 128:256] = 0x0001                           # whole groups of the smallest subnormal
     for p2, sf in VARIANTS:
         check(x, 16, dt, p2, sf, label="extremes")
         check(x, 128, dt, p2, sf, label="extremes")

@@ -1,0 +1,59 @@
+"""CPU checks of facts the gfx950 kernels rely on (no GPU, no oracle code):
+the silu32 table's closed-form regions and its rounding margin."""
+from __future__ import annotations
+
+import decimal
+from fractions import Fraction
+
+import numpy as np
+
+import libref
+from exact import floor_log2
+
+# design constants of the SwiGLU kernel's table (bf16 magnitude bits)
+SILU_LO, SILU_HI = 0x3280, 0x4300          # 2^-26 and 128
+
+
+def _bf16(bits):
+    return float(np.array([bits << 16], np.uint32).view(np.float32)[0])
+
+
+def test_closed_forms_outside_the_table():
+    table = libref.silu32_table()                        # 60-digit reference
+    for b in range(65536):
+        if (b & 0x7F80) == 0x7F80:
+            continue
+        mag, neg = b & 0x7FFF, b >> 15
+        g = np.float32(_bf16(b))
+        want = table[b].view(np.uint32)
+        if mag < SILU_LO:
+            assert (g * np.float32(0.5)).view(np.uint32) == want, hex(b)
+        elif mag > SILU_HI:
+            expect = np.float32(-0.0) if neg else g
+            assert expect.view(np.uint32) == want, hex(b)
+
+
+def test_table_values_keep_a_margin_from_fp32_midpoints():
+    """For 2^-6 <= |g| <= 128 the exact silu(g) never comes within 2^-20 fp32
+    ulp of a point halfway between two fp32 values (subnormal results
+    included), while an fp64 evaluation errs by under 2^-26 fp32 ulp; so one
+    fp64 -> fp32 rounding gives the correctly rounded value."""
+    ctx = decimal.Context(prec=50, Emax=10**6, Emin=-10**6)
+    worst = 1.0
+    for mag in range(SILU_LO, SILU_HI + 1):
+        for neg in (0, 1):
+            g = _bf16((neg << 15) | mag)
+            if abs(g) < 2.0 ** -6:
+                continue
+            dg = decimal.Decimal(g)
+            v = Fraction(ctx.divide(dg, ctx.add(1, ctx.exp(-dg))))
+            av = abs(v)
+            if av < Fraction(2) ** -151:
+                continue                  # below a quarter of the smallest subnormal: rounds to -0 by far
+            e = max(floor_log2(av), -126)
+            ulp = Fraction(2) ** (e - 23)
+            k = av / ulp                          # position in ulps
+            frac = k - (k.numerator // k.denominator)
+            worst = min(worst, float(abs(frac - Fraction(1, 2))))
+    assert worst > 2.0 ** -20, worst
+
