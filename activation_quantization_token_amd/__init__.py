@@ -9,12 +9,14 @@ from .binding import (  # noqa: F401
     QDTYPES,
     SCALE_FMTS,
     TkError,
+    copy_stream,
     empty_outputs,
     load_library,
     per_token_cast,
     silu32_bf16,
     swiglu_per_token_cast,
     tk_abi_version,
+    tk_copy_stream,
     tk_per_token_cast,
     tk_prepare_device,
     tk_silu32_bf16,

@@ -54,6 +54,8 @@ def load_library(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         lib.tk_silu32_bf16.argtypes = [vp, vp, i64, vp]
         lib.tk_silu32_bf16.restype = ctypes.c_int
+        lib.tk_copy_stream.argtypes = [vp, vp, i64, vp]
+        lib.tk_copy_stream.restype = ctypes.c_int
         lib.tk_prepare_device.argtypes = []
         lib.tk_prepare_device.restype = ctypes.c_int
         lib.tk_status_string.argtypes = [i32]
@@ -102,6 +104,22 @@ def silu32_bf16(g: torch.Tensor, stream=None) -> torch.Tensor:
     out = torch.empty(g.shape, dtype=torch.float32, device=g.device)
     _check(tk_silu32_bf16(g.data_ptr(), out.data_ptr(), g.numel(), _stream_handle(stream, g.device)))
     return out
+
+
+def tk_copy_stream(src: int, dst: int, nbytes: int, stream: int) -> int:
+    """Raw C call: streaming copy of nbytes (diagnostic); returns the tk_status code."""
+    return load_library().tk_copy_stream(src, dst, nbytes, stream)
+
+
+def copy_stream(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Diagnostic: byte copy src -> dst with the cast's streaming memory instructions."""
+    for t in (src, dst):
+        if not t.is_cuda or not t.is_contiguous():
+            raise TypeError("src and dst must be contiguous GPU tensors")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    _check(tk_copy_stream(src.data_ptr(), dst.data_ptr(), n, _stream_handle(stream, src.device)))
 
 
 def tk_per_token_cast(x: int, rows: int, cols: int, x_ld: int, q: int, q_ld: int, scales: int,

@@ -15,9 +15,12 @@
 // instruction reads 1 KiB contiguously.  Every group size divides 512, and a
 // group of G columns is G/8 consecutive lanes of one DPP row (16 lanes), so
 // the group amax is a 1..4-step DPP butterfly with no LDS and no barrier.
-// All U segments are loaded before any is converted, to keep U KiB per wave
-// in flight.  Codes are written with one 8-byte (E4M3) or 4-byte (E2M1)
-// store per lane, i.e. 512 or 256 contiguous bytes per wave instruction.
+// All U segments are loaded before any is converted.  Codes are written with
+// one 8-byte (E4M3) or 4-byte (E2M1) store per lane, i.e. 512 or 256
+// contiguous bytes per wave instruction.  Rows are addressed through buffer
+// resource descriptors whose size is the row's length, so loads past the row
+// end return zero and stores past it are dropped by the hardware: ragged
+// tails need no predication.  All global traffic is non-temporal.
 
 #include <hip/hip_runtime.h>
 
@@ -31,8 +34,6 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int kSegCols = kWave * 8;   // columns per wave per segment
 
 constexpr int kE4M3 = TK_QDTYPE_E4M3;
@@ -49,6 +50,36 @@ struct CastParams {
     int64_t s_ld;
 };
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Buffer access.  dword 3 of a gfx9-family buffer descriptor is 0x00020000
+// for raw (untyped, unswizzled) access; cache policy 2 sets the non-temporal
+// bit (nt), so streamed lines do not displace other data in L2 / the Infinity
+// Cache and a call's writes do not linger as dirty lines.
+
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), kBufferDword3);
+}
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, int(byte_off), 0, kNonTemporal);
+}
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, int(byte_off), 0, kNonTemporal);
+}
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x2 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, int(byte_off), 0, kNonTemporal);
+}
+
 // ---------------------------------------------------------------------------
 // silu32 table.  silu32(g) = fp32 nearest to g / (1 + e^-g) is needed exactly
 // (correctly rounded) for every bf16 gate.  Outside |g| in [2^-26, 128] it has
@@ -58,11 +89,16 @@ struct CastParams {
 //                fp32 value, so silu32(g) = g * 0.5f.
 //   g > 128:     g - silu(g) = g e^-g / (1 + e^-g) < g 2^-184: rounds to g.
 //   g < -128:    |silu(g)| < |g| e^g < 2^-150 for all such g: rounds to -0.
-// Inside, the value comes from a table indexed by the bf16 magnitude and sign,
-// built once per device by silu_table_kernel in fp64 and rounded once to fp32.
+// Inside, the value comes from a table indexed by (bf16 magnitude, sign),
+// built once per device by silu_table_kernel in fp64 and rounded once to
+// fp32.  Entry 0 and the last entry hold a NaN: the fast lookup clamps the
+// index onto them for gates outside the table, and the NaN then flags the
+// group for the exact (closed-form) path.
 constexpr uint32_t kSiluLo = 0x3280;   // bf16 magnitude bits of 2^-26
 constexpr uint32_t kSiluHi = 0x4300;   // bf16 magnitude bits of 128
-constexpr int kSiluEntries = 2 * int(kSiluHi - kSiluLo + 1);   // sign interleaved
+constexpr int kSiluValues = 2 * int(kSiluHi - kSiluLo + 1);
+constexpr int kSiluEntries = kSiluValues + 2;
+constexpr uint32_t kSentinel = 0x7FC00000u;   // quiet NaN
 
 __device__ float g_silu_table[kSiluEntries];
 
@@ -99,8 +135,13 @@ __global__ void silu_table_kernel()
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= kSiluEntries) return;
-    const uint32_t mag = kSiluLo + uint32_t(i >> 1);
-    const uint32_t bits = (uint32_t(i & 1) << 15) | mag;
+    if (i == 0 || i == kSiluEntries - 1) {
+        g_silu_table[i] = __uint_as_float(kSentinel);
+        return;
+    }
+    const int j = i - 1;
+    const uint32_t mag = kSiluLo + uint32_t(j >> 1);
+    const uint32_t bits = (uint32_t(j & 1) << 15) | mag;
     const double g = double(__uint_as_float(bits << 16));
     float r;
     if (fabs(g) < 0x1p-6) {
@@ -115,6 +156,34 @@ __global__ void silu_table_kernel()
         r = float((g * e) / (1.0 + e));
     }
     g_silu_table[i] = r;
+}
+
+// Byte offsets into the table for the two bf16 gates packed in w, with packed
+// 16-bit integer ops: index = clamp((mag << 1 | sign) - (2 Lo - 1), 0, last).
+// Gates below the table land on entry 0, gates above it on the last entry.
+__device__ __forceinline__ u16x2 silu_offsets(uint32_t w)
+{
+    const u16x2 h = __builtin_bit_cast(u16x2, w);
+    const u16x2 key = (h << (unsigned short)1) | (h >> (unsigned short)15);
+    const u16x2 idx = __builtin_elementwise_min(
+        __builtin_elementwise_sub_sat(key, u16x2((unsigned short)(2 * kSiluLo - 1))),
+        u16x2((unsigned short)(kSiluEntries - 1)));
+    return idx << (unsigned short)2;
+}
+
+__device__ __forceinline__ float table_at(const float *tab, unsigned short byte_off)
+{
+    return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(tab) + byte_off);
+}
+
+// The closed forms outside the table, for the rare exact path.
+__device__ float silu32_exact(uint32_t b, const float *tab)
+{
+    const uint32_t mag = b & 0x7FFFu, neg = (b >> 15) & 1u;
+    const float g = __uint_as_float(b << 16);
+    if (mag < kSiluLo) return g * 0.5f;
+    if (mag > kSiluHi) return neg ? -0.0f : g;
+    return tab[1 + 2 * (mag - kSiluLo) + neg];
 }
 
 // ---------------------------------------------------------------------------
@@ -148,11 +217,11 @@ __device__ __forceinline__ uint32_t shfl_u32(uint32_t v, int src_lane)
 
 // ---------------------------------------------------------------------------
 // The per-segment cast: 8 fp32 values per lane (columns col .. col+7 of one
-// row), their |max| bits, the row's output pointers.
+// row), their |max| bits, and buffer descriptors of the row's codes and scales.
 
 template <int G, int QD, bool POW2, int SF>
-__device__ __forceinline__ void cast_segment(const float (&x)[8], uint32_t amax_bits, bool valid,
-                                             int lane, int64_t col, uint8_t *qrow, void *srow)
+__device__ __forceinline__ void cast_segment(const float (&x)[8], uint32_t amax_bits, int lane, uint32_t col,
+                                             __amdgpu_buffer_rsrc_t qrow, __amdgpu_buffer_rsrc_t srow)
 {
     constexpr float D = (QD == kE4M3) ? 448.0f : 6.0f;
     amax_bits = group_max<G>(amax_bits);
@@ -176,161 +245,208 @@ __device__ __forceinline__ void cast_segment(const float (&x)[8], uint32_t amax_
         v[i] = POW2 ? x[i] * inv : x[i] / s;
         v[i] = __builtin_amdgcn_fmed3f(v[i], D, -D);
     }
-    if (valid) {
-        if constexpr (QD == kE4M3) {
-            uint32_t lo = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false));
-            lo = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], int(lo), true));
-            uint32_t hi = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false));
-            hi = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], int(hi), true));
-            *reinterpret_cast<uint2 *>(qrow + col) = make_uint2(lo, hi);
-        } else {
-            uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
-            r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], 1.0f, 1);
-            r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], 1.0f, 2);
-            r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], 1.0f, 3);
-            *reinterpret_cast<uint32_t *>(qrow + col / 2) = r;
-        }
+    if constexpr (QD == kE4M3) {
+        uint32_t lo = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false));
+        lo = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], int(lo), true));
+        uint32_t hi = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false));
+        hi = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], int(hi), true));
+        store8(qrow, col, u32x2{lo, hi});
+    } else {
+        uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], 1.0f, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], 1.0f, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], 1.0f, 3);
+        store4(qrow, col / 2, r);
     }
     constexpr int kLanesPerGroup = G / 8;
     if constexpr (SF == kScaleF32) {
-        if (valid && (lane % kLanesPerGroup) == 0)
-            static_cast<float *>(srow)[col / G] = s;
+        if ((lane % kLanesPerGroup) == 0) store4(srow, (col / G) * 4, __float_as_uint(s));
     } else {
         // Four consecutive groups' exponent bytes -> one little-endian int32,
         // written by the first lane of the first group.
         const uint32_t b1 = shfl_u32(e8, lane + kLanesPerGroup);
         const uint32_t b2 = shfl_u32(e8, lane + 2 * kLanesPerGroup);
         const uint32_t b3 = shfl_u32(e8, lane + 3 * kLanesPerGroup);
-        if (valid && (lane % (4 * kLanesPerGroup)) == 0)
-            static_cast<uint32_t *>(srow)[col / (4 * G)] = e8 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        if ((lane % (4 * kLanesPerGroup)) == 0)
+            store4(srow, (col / (4 * G)) * 4, e8 | (b1 << 8) | (b2 << 16) | (b3 << 24));
     }
 }
 
-__device__ __forceinline__ void widen8(const uint4 &w, float (&x)[8])
+__device__ __forceinline__ void widen8(const u32x4 &w, float (&x)[8])
 {
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        x[2 * k] = __uint_as_float(ws[k] << 16);
-        x[2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
+        x[2 * k] = __uint_as_float(w[k] << 16);
+        x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
     }
 }
 
 // |x| max of 8 bf16 as fp32 bits: bf16 magnitudes compare as unsigned 16-bit
 // integers, two per packed max.
-__device__ __forceinline__ uint32_t amax_bits_bf16x8(const uint4 &w)
+__device__ __forceinline__ uint32_t amax_bits_bf16x8(const u32x4 &w)
 {
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     const uint32_t m = 0x7FFF7FFFu;
-    const uint32_t a = w.x & m, b = w.y & m, c = w.z & m, d = w.w & m;
-    u16x2 va = __builtin_bit_cast(u16x2, a), vb = __builtin_bit_cast(u16x2, b);
-    u16x2 vc = __builtin_bit_cast(u16x2, c), vd = __builtin_bit_cast(u16x2, d);
-    u16x2 t = __builtin_elementwise_max(__builtin_elementwise_max(va, vb),
-                                        __builtin_elementwise_max(vc, vd));
+    const u16x2 va = __builtin_bit_cast(u16x2, uint32_t(w[0] & m)), vb = __builtin_bit_cast(u16x2, uint32_t(w[1] & m));
+    const u16x2 vc = __builtin_bit_cast(u16x2, uint32_t(w[2] & m)), vd = __builtin_bit_cast(u16x2, uint32_t(w[3] & m));
+    const u16x2 t = __builtin_elementwise_max(__builtin_elementwise_max(va, vb), __builtin_elementwise_max(vc, vd));
     const uint32_t lo = t.x, hi = t.y;
     return max(lo, hi) << 16;
 }
 
 // ---------------------------------------------------------------------------
-// Kernels.  Work unit = (row, run of U segments); a wave takes units in a
-// grid-stride loop (the unit index is wave-uniform, so DPP and bpermute always
-// run with every lane active; lanes past the row end only skip their stores).
+// Work decomposition.  A row has nseg = ceil(cols / 512) segments, grouped in
+// runs of U; a work unit is one (row, run).  Units are numbered row-major and
+// handed out in order, so the waves resident at any moment cover one compact
+// address window (the DRAM pages of a few consecutive rows), which measured
+// faster than giving each workgroup its own distant stretch of rows.
 
-template <int G, int QD, bool POW2, int SF, int U>
-__global__ __launch_bounds__(kBlock) void cast_kernel(CastParams p)
+struct Unit {
+    int64_t row;
+    uint32_t col0;   // first column of this lane in the run
+};
+
+template <int U>
+__device__ __forceinline__ Unit decode_unit(int64_t unit, int64_t runs, int lane)
+{
+    int64_t row, run;
+    if (unit <= int64_t(0xFFFFFFFF) && runs <= int64_t(0xFFFFFFFF)) {   // 32-bit division
+        const uint32_t u32 = uint32_t(unit), r32 = uint32_t(runs);
+        row = u32 / r32;
+        run = u32 - uint32_t(row) * r32;
+    } else {
+        row = unit / runs;
+        run = unit - row * runs;
+    }
+    return Unit{row, uint32_t(run) * uint32_t(U * kSegCols) + uint32_t(lane) * 8u};
+}
+
+// Descriptors of one row's codes and scales, sized to exactly that row.
+template <int G, int QD, int SF>
+__device__ __forceinline__ void output_rows(const CastParams &p, int64_t row, __amdgpu_buffer_rsrc_t &qrow,
+                                            __amdgpu_buffer_rsrc_t &srow)
+{
+    const uint32_t cols = uint32_t(p.cols);
+    qrow = row_buffer(p.q + row * p.q_ld, QD == kE4M3 ? cols : cols / 2);
+    if constexpr (SF == kScaleF32)
+        srow = row_buffer(static_cast<float *>(p.s) + row * p.s_ld, (cols / G) * 4u);
+    else
+        srow = row_buffer(static_cast<uint32_t *>(p.s) + row * p.s_ld, cols / G);
+}
+
+// ---------------------------------------------------------------------------
+// Kernels.  A wave takes units in a grid-stride loop (one unit per wave when
+// the grid covers all units).  The unit index is wave-uniform, so DPP and
+// bpermute always run with every lane active.
+
+template <int G, int QD, bool POW2, int SF, int U, int WPB>
+__global__ __launch_bounds__(kWave * WPB) void cast_kernel(CastParams p)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    const int64_t nwaves = int64_t(gridDim.x) * kWavesPerBlock;
+    // threadIdx.x >> 6 is the same on every lane of a wave; readfirstlane tells
+    // the compiler so, which keeps the row descriptors in scalar registers.
+    const int64_t wave = int64_t(blockIdx.x) * WPB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = int64_t(gridDim.x) * WPB;
     const int64_t nseg = (p.cols + kSegCols - 1) / kSegCols;
     const int64_t runs = (nseg + U - 1) / U;
     const int64_t units = p.rows * runs;
     for (int64_t unit = wave; unit < units; unit += nwaves) {
-        const int64_t row = unit / runs;
-        const int64_t col0 = (unit - row * runs) * U * kSegCols + lane * 8;
-        const uint16_t *xrow = p.x + row * p.x_ld;
-        uint4 w[U];
+        const Unit un = decode_unit<U>(unit, runs, lane);
+        const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + un.row * p.x_ld, uint32_t(p.cols) * 2u);
+        u32x4 w[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) w[k] = load16(xrow, (un.col0 + k * kSegCols) * 2u);
+        __amdgpu_buffer_rsrc_t qrow, srow;
+        output_rows<G, QD, SF>(p, un.row, qrow, srow);
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const int64_t col = col0 + k * kSegCols;
-            w[k] = (col < p.cols) ? *reinterpret_cast<const uint4 *>(xrow + col) : make_uint4(0, 0, 0, 0);
-        }
-        uint8_t *qrow = p.q + row * p.q_ld;
-        void *srow = (SF == kScaleF32) ? static_cast<void *>(static_cast<float *>(p.s) + row * p.s_ld)
-                                       : static_cast<void *>(static_cast<uint32_t *>(p.s) + row * p.s_ld);
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int64_t col = col0 + k * kSegCols;
             float x[8];
             widen8(w[k], x);
-            cast_segment<G, QD, POW2, SF>(x, amax_bits_bf16x8(w[k]), col < p.cols, lane, col, qrow, srow);
+            cast_segment<G, QD, POW2, SF>(x, amax_bits_bf16x8(w[k]), lane, un.col0 + k * kSegCols, qrow, srow);
         }
     }
 }
 
-__device__ __forceinline__ float silu32_lookup(uint32_t gbits, float g, const float *tab)
-{
-    const uint32_t mag = gbits & 0x7FFFu;
-    const uint32_t neg = (gbits >> 15) & 1u;
-    const uint32_t m = min(max(mag, kSiluLo), kSiluHi);
-    const float t = tab[2 * (m - kSiluLo) + neg];
-    float r = (mag < kSiluLo) ? g * 0.5f : t;
-    r = (mag > kSiluHi) ? (neg ? -0.0f : g) : r;
-    return r;
-}
+constexpr int kSiluBlock = 256;
 
-__global__ __launch_bounds__(kBlock) void silu32_kernel(const uint16_t *g, float *out, int64_t n)
+// Diagnostic: silu32 of n bf16 gates (two per thread) through the same fast
+// lookup + exact path as the fused kernel.
+__global__ __launch_bounds__(kSiluBlock) void silu32_kernel(const uint16_t *g, float *out, int64_t n)
 {
-    const int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+    const int64_t i = 2 * (int64_t(blockIdx.x) * kSiluBlock + threadIdx.x);
     if (i >= n) return;
-    const uint32_t b = g[i];
-    out[i] = silu32_lookup(b, __uint_as_float(b << 16), g_silu_table);
+    const uint32_t b0 = g[i], b1 = (i + 1 < n) ? g[i + 1] : 0u;
+    const u16x2 off = silu_offsets(b0 | (b1 << 16));
+    float r0 = table_at(g_silu_table, off.x), r1 = table_at(g_silu_table, off.y);
+    if (__float_as_uint(r0) == kSentinel) r0 = silu32_exact(b0, g_silu_table);
+    if (__float_as_uint(r1) == kSentinel) r1 = silu32_exact(b1, g_silu_table);
+    out[i] = r0;
+    if (i + 1 < n) out[i + 1] = r1;
 }
 
-template <int G, int QD, bool POW2, int SF, int U>
-__global__ __launch_bounds__(kBlock) void swiglu_cast_kernel(CastParams p)
+constexpr int kCopyBlock = 256;
+
+__global__ __launch_bounds__(kCopyBlock) void copy_stream_kernel(const u32x4 *src, u32x4 *dst, int64_t n16)
+{
+    const int64_t stride = int64_t(gridDim.x) * kCopyBlock;
+    for (int64_t i = int64_t(blockIdx.x) * kCopyBlock + threadIdx.x; i < n16; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+template <int G, int QD, bool POW2, int SF, int U, int WPB>
+__global__ __launch_bounds__(kWave * WPB) void swiglu_cast_kernel(CastParams p)
 {
     __shared__ float tab[kSiluEntries];
-    for (int i = threadIdx.x; i < kSiluEntries; i += kBlock) tab[i] = g_silu_table[i];
+    for (int i = threadIdx.x; i < kSiluEntries; i += kWave * WPB) tab[i] = g_silu_table[i];
     __syncthreads();
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    const int64_t nwaves = int64_t(gridDim.x) * kWavesPerBlock;
+    // threadIdx.x >> 6 is the same on every lane of a wave; readfirstlane tells
+    // the compiler so, which keeps the row descriptors in scalar registers.
+    const int64_t wave = int64_t(blockIdx.x) * WPB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = int64_t(gridDim.x) * WPB;
     const int64_t nseg = (p.cols + kSegCols - 1) / kSegCols;
     const int64_t runs = (nseg + U - 1) / U;
     const int64_t units = p.rows * runs;
+    const uint32_t half_bytes = uint32_t(p.cols) * 2u;
     for (int64_t unit = wave; unit < units; unit += nwaves) {
-        const int64_t row = unit / runs;
-        const int64_t col0 = (unit - row * runs) * U * kSegCols + lane * 8;
-        const uint16_t *grow = p.x + row * p.x_ld;
-        const uint16_t *urow = grow + p.cols;
-        uint4 wg[U], wu[U];
+        const Unit un = decode_unit<U>(unit, runs, lane);
+        const uint16_t *grow = p.x + un.row * p.x_ld;
+        const __amdgpu_buffer_rsrc_t gate = row_buffer(grow, half_bytes);
+        const __amdgpu_buffer_rsrc_t up = row_buffer(grow + p.cols, half_bytes);
+        u32x4 wg[U], wu[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const int64_t col = col0 + k * kSegCols;
-            const bool ok = col < p.cols;
-            wg[k] = ok ? *reinterpret_cast<const uint4 *>(grow + col) : make_uint4(0, 0, 0, 0);
-            wu[k] = ok ? *reinterpret_cast<const uint4 *>(urow + col) : make_uint4(0, 0, 0, 0);
+            wg[k] = load16(gate, (un.col0 + k * kSegCols) * 2u);
+            wu[k] = load16(up, (un.col0 + k * kSegCols) * 2u);
         }
-        uint8_t *qrow = p.q + row * p.q_ld;
-        void *srow = (SF == kScaleF32) ? static_cast<void *>(static_cast<float *>(p.s) + row * p.s_ld)
-                                       : static_cast<void *>(static_cast<uint32_t *>(p.s) + row * p.s_ld);
+        __amdgpu_buffer_rsrc_t qrow, srow;
+        output_rows<G, QD, SF>(p, un.row, qrow, srow);
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const int64_t col = col0 + k * kSegCols;
-            float g[8], u[8], h[8];
-            widen8(wg[k], g);
+            float u[8], h[8];
             widen8(wu[k], u);
-            const uint32_t gw[4] = {wg[k].x, wg[k].y, wg[k].z, wg[k].w};
             uint32_t amax = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t gb = (i & 1) ? (gw[i / 2] >> 16) : (gw[i / 2] & 0xFFFFu);
-                h[i] = silu32_lookup(gb, g[i], tab) * u[i];
-                amax = max(amax, __float_as_uint(h[i]) & 0x7FFFFFFFu);
+            for (int j = 0; j < 4; ++j) {
+                const u16x2 off = silu_offsets(wg[k][j]);
+                h[2 * j] = table_at(tab, off.x) * u[2 * j];
+                h[2 * j + 1] = table_at(tab, off.y) * u[2 * j + 1];
+                amax = max(amax, max(__float_as_uint(h[2 * j]) & 0x7FFFFFFFu,
+                                     __float_as_uint(h[2 * j + 1]) & 0x7FFFFFFFu));
             }
-            cast_segment<G, QD, POW2, SF>(h, amax, col < p.cols, lane, col, qrow, srow);
+            // A NaN from a sentinel entry (a gate outside the table) makes the
+            // bits exceed every finite magnitude; such segments, rare and
+            // wave-uniform, take the exact path.
+            if (__builtin_amdgcn_ballot_w64(amax > 0x7F7FFFFFu) != 0) {
+                amax = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t gb = (i & 1) ? (wg[k][i / 2] >> 16) : (wg[k][i / 2] & 0xFFFFu);
+                    h[i] = silu32_exact(gb, tab) * u[i];
+                    amax = max(amax, __float_as_uint(h[i]) & 0x7FFFFFFFu);
+                }
+            }
+            cast_segment<G, QD, POW2, SF>(h, amax, lane, un.col0 + k * kSegCols, qrow, srow);
         }
     }
 }
@@ -395,6 +511,7 @@ tk_status validate(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void
     const int64_t q_cols = (out_dtype == kE4M3) ? cols : cols / 2;
     const int64_t s_cols = (scale_fmt == kScaleF32) ? ngroups : ngroups / 4;
     if (x_ld < in_cols || q_ld < q_cols || s_ld < s_cols) return TK_ERROR_INVALID_VALUE;
+    if (in_cols >= (int64_t(1) << 29)) return TK_ERROR_UNSUPPORTED;   // row byte offsets are 32-bit
     if (rows == 0) return TK_SUCCESS;
     if (!x || !q || !scales) return TK_ERROR_INVALID_VALUE;
     if (!aligned(x, 16) || (x_ld * 2) % 16 != 0) return TK_ERROR_MISALIGNED;
@@ -406,39 +523,47 @@ tk_status validate(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void
 
 using KernelFn = void (*)(CastParams);
 
+// Launch shape of each kernel family (measured on MI355X over the cast's
+// workloads): U segments (U KiB of bf16 per wave per unit) and WPB waves per
+// workgroup.  The plain cast runs one unit per wave; the SwiGLU form keeps a
+// bounded grid so that each workgroup's copy of the silu32 table into LDS
+// serves many units.
+constexpr int kCastU = 2, kCastWPB = 2;
+constexpr int kSwigluU = 2, kSwigluWPB = 8, kSwigluBlocksPerCU = 4;
+
 // Kernel pointers by [group index][out dtype][variant]; variant 0 = plain
 // fp32 scale, 1 = power-of-two fp32 scale, 2 = power-of-two UE8M0 x4.
 struct KernelTable {
     KernelFn fn[4][2][3];
 };
 
-template <bool SWIGLU, int G, int QD, bool POW2, int SF, int U>
+template <bool SWIGLU, int G, int QD, bool POW2, int SF>
 constexpr KernelFn pick()
 {
-    if constexpr (SWIGLU) return swiglu_cast_kernel<G, QD, POW2, SF, U>;
-    else return cast_kernel<G, QD, POW2, SF, U>;
+    if constexpr (SWIGLU) return swiglu_cast_kernel<G, QD, POW2, SF, kSwigluU, kSwigluWPB>;
+    else return cast_kernel<G, QD, POW2, SF, kCastU, kCastWPB>;
 }
 
-template <bool SWIGLU, int G, int QD, int U>
+template <bool SWIGLU, int G, int QD>
 void fill_variants(KernelFn (&t)[3])
 {
-    t[0] = pick<SWIGLU, G, QD, false, kScaleF32, U>();
-    t[1] = pick<SWIGLU, G, QD, true, kScaleF32, U>();
-    t[2] = pick<SWIGLU, G, QD, true, kScaleUE8M0, U>();
+    t[0] = pick<SWIGLU, G, QD, false, kScaleF32>();
+    t[1] = pick<SWIGLU, G, QD, true, kScaleF32>();
+    t[2] = pick<SWIGLU, G, QD, true, kScaleUE8M0>();
 }
 
-template <bool SWIGLU, int U>
+template <bool SWIGLU>
 KernelTable make_table()
 {
     KernelTable t;
-    fill_variants<SWIGLU, 16, kE4M3, U>(t.fn[0][0]);
-    fill_variants<SWIGLU, 16, kE2M1, U>(t.fn[0][1]);
-    fill_variants<SWIGLU, 32, kE4M3, U>(t.fn[1][0]);
-    fill_variants<SWIGLU, 32, kE2M1, U>(t.fn[1][1]);
-    fill_variants<SWIGLU, 64, kE4M3, U>(t.fn[2][0]);
-    fill_variants<SWIGLU, 64, kE2M1, U>(t.fn[2][1]);
-    fill_variants<SWIGLU, 128, kE4M3, U>(t.fn[3][0]);
-    fill_variants<SWIGLU, 128, kE2M1, U>(t.fn[3][1]);
+    fill_variants<SWIGLU, 16, kE4M3>(t.fn[0][0]);
+    fill_variants<SWIGLU, 16, kE2M1>(t.fn[0][1]);
+    fill_variants<SWIGLU, 32, kE4M3>(t.fn[1][0]);
+    fill_variants<SWIGLU, 32, kE2M1>(t.fn[1][1]);
+    fill_variants<SWIGLU, 64, kE4M3>(t.fn[2][0]);
+    fill_variants<SWIGLU, 64, kE2M1>(t.fn[2][1]);
+    fill_variants<SWIGLU, 128, kE4M3>(t.fn[3][0]);
+    fill_variants<SWIGLU, 128, kE2M1>(t.fn[3][1]);
     return t;
 }
 
@@ -461,35 +586,22 @@ tk_status launch(bool swiglu, const void *x, int64_t rows, int64_t cols, int64_t
         if (st != TK_SUCCESS) return st;
     }
 
+    static const KernelTable cast_table = make_table<false>();
+    static const KernelTable swiglu_table = make_table<true>();
     const int variant = !round_pow2 ? 0 : (scale_fmt == kScaleF32 ? 1 : 2);
-    const int gi = group_index(group);
+    const KernelFn fn = (swiglu ? swiglu_table : cast_table).fn[group_index(group)][out_dtype][variant];
+    const int U = swiglu ? kSwigluU : kCastU;
+    const int wpb = swiglu ? kSwigluWPB : kCastWPB;
     const int64_t nseg = (cols + kSegCols - 1) / kSegCols;
-    KernelFn fn;
-    int U;
-    if (!swiglu) {
-        static const KernelTable t1 = make_table<false, 1>();
-        static const KernelTable t4 = make_table<false, 4>();
-        static const KernelTable t7 = make_table<false, 7>();
-        if (nseg % 7 == 0) { fn = t7.fn[gi][out_dtype][variant]; U = 7; }
-        else if (nseg >= 4) { fn = t4.fn[gi][out_dtype][variant]; U = 4; }
-        else { fn = t1.fn[gi][out_dtype][variant]; U = 1; }
-    } else {
-        static const KernelTable t1 = make_table<true, 1>();
-        static const KernelTable t4 = make_table<true, 4>();
-        if (nseg >= 4) { fn = t4.fn[gi][out_dtype][variant]; U = 4; }
-        else { fn = t1.fn[gi][out_dtype][variant]; U = 1; }
-    }
     const int64_t units = rows * ((nseg + U - 1) / U);
-    int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-    // SwiGLU blocks first copy the silu32 table into LDS: keep the grid near
-    // two resident blocks per CU so that copy is amortised over many rows.
-    const int64_t cap = swiglu ? int64_t(info->cus) * 2 : int64_t(1) << 30;
-    if (blocks > cap) blocks = cap;
+    int64_t blocks = (units + wpb - 1) / wpb;
+    const int64_t cap = swiglu ? int64_t(info->cus) * kSwigluBlocksPerCU : int64_t(0x7FFFFFFF);
+    if (blocks > cap) blocks = cap;     // the kernels loop over the remaining units
     CastParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld,
                  scales, s_ld};
     void *args[] = {&p};
-    if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kBlock), args, 0, s)
-        != hipSuccess)
+    if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * wpb), args,
+                        0, s) != hipSuccess)
         return TK_ERROR_LAUNCH;
     return TK_SUCCESS;
 }
@@ -531,10 +643,32 @@ tk_status tk_silu32_bf16(const void *g, void *out, int64_t n, void *stream)
     const uint16_t *gp = static_cast<const uint16_t *>(g);
     float *op = static_cast<float *>(out);
     void *args[] = {&gp, &op, &n};
-    const int64_t blocks = (n + kBlock - 1) / kBlock;
+    const int64_t blocks = ((n + 1) / 2 + kSiluBlock - 1) / kSiluBlock;
     if (blocks > int64_t(0x7FFFFFFF)) return TK_ERROR_INVALID_VALUE;
-    if (hipLaunchKernel(reinterpret_cast<const void *>(silu32_kernel), dim3(uint32_t(blocks)), dim3(kBlock),
+    if (hipLaunchKernel(reinterpret_cast<const void *>(silu32_kernel), dim3(uint32_t(blocks)), dim3(kSiluBlock),
                         args, 0, s) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    return TK_SUCCESS;
+}
+
+tk_status tk_copy_stream(const void *src, void *dst, int64_t bytes, void *stream)
+{
+    if (bytes < 0 || bytes % 16 != 0) return TK_ERROR_INVALID_VALUE;
+    if (bytes == 0) return TK_SUCCESS;
+    if (!src || !dst) return TK_ERROR_INVALID_VALUE;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return TK_ERROR_MISALIGNED;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    tk_status st = device_info(&dev, &info);
+    if (st != TK_SUCCESS) return st;
+    const u32x4 *sp = static_cast<const u32x4 *>(src);
+    u32x4 *dp = static_cast<u32x4 *>(dst);
+    int64_t n16 = bytes / 16;
+    int64_t blocks = (n16 + kCopyBlock - 1) / kCopyBlock;
+    if (blocks > int64_t(info->cus) * 128) blocks = int64_t(info->cus) * 128;
+    void *args[] = {&sp, &dp, &n16};
+    if (hipLaunchKernel(reinterpret_cast<const void *>(copy_stream_kernel), dim3(uint32_t(blocks)),
+                        dim3(kCopyBlock), args, 0, static_cast<hipStream_t>(stream)) != hipSuccess)
         return TK_ERROR_LAUNCH;
     return TK_SUCCESS;
 }

@@ -122,6 +122,16 @@ tk_status tk_swiglu_per_token_cast(const void *gate_up, int64_t rows, int64_t co
 tk_status tk_silu32_bf16(const void *g, void *out, int64_t n, void *stream);
 
 /*
+ * tk_copy_stream -- diagnostic: copy `bytes` bytes from src to dst with the
+ * cast's memory instructions (16-byte non-temporal loads and stores, one pass,
+ * grid-stride).  Used to calibrate hardware memory counters against a
+ * transfer of known size and to measure the practical streaming ceiling.
+ * src, dst: device pointers, 16-byte aligned, non-overlapping; bytes >= 0 and
+ * a multiple of 16 (TK_ERROR_INVALID_VALUE / TK_ERROR_MISALIGNED otherwise).
+ */
+tk_status tk_copy_stream(const void *src, void *dst, int64_t bytes, void *stream);
+
+/*
  * tk_prepare_device -- build the per-device tables used by the SwiGLU form on
  * the current HIP device, and wait until they are ready.  Idempotent; safe to
  * call from several threads.

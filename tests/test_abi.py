@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("tk_per_token_cast", "tk_swiglu_per_token_cast", "tk_status_string", "tk_abi_version",
-              "tk_prepare_device", "tk_silu32_bf16"):
+              "tk_prepare_device", "tk_silu32_bf16", "tk_copy_stream"):
         assert n in names
 
 
@@ -107,6 +107,14 @@ def test_silu_diagnostic_validation():
     assert tk.tk_silu32_bf16(0, Q, 5, 0) == INVALID
     assert tk.tk_silu32_bf16(X + 1, Q, 5, 0) == MISALIGNED
     assert tk.tk_silu32_bf16(X, Q + 2, 5, 0) == MISALIGNED
+
+
+def test_copy_stream_validation():
+    assert tk.tk_copy_stream(X, Q, -16, 0) == INVALID
+    assert tk.tk_copy_stream(X, Q, 24, 0) == INVALID
+    assert tk.tk_copy_stream(X, Q, 0, 0) == 0
+    assert tk.tk_copy_stream(0, Q, 32, 0) == INVALID
+    assert tk.tk_copy_stream(X + 8, Q, 32, 0) == MISALIGNED
 
 
 def test_binding_rejects_cpu_tensors():

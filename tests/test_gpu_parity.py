@@ -239,6 +239,15 @@ def test_many_rows_narrow():
     check(x, 64, "e4m3", False, "f32", guard=False, label="many-rows")
 
 
+def test_copy_stream_copies():
+    log("[gpu] streaming copy diagnostic")
+    src = torch.randint(0, 256, (3 << 20,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    tk.copy_stream(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+
+
 def test_side_stream_and_reuse():
     log("[gpu] side stream")
     x_bits = inputs.generate_small(1, 64, 7168)
