@@ -80,6 +80,17 @@ __device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t byte_o
     __builtin_amdgcn_raw_buffer_store_b64(v, r, int(byte_off), 0, kNonTemporal);
 }
 
+// Scale rows are short (4 to 2048 bytes) and each is written in 4-to-64-byte
+// pieces by several waves; plain write-back stores let L2 merge those pieces
+// into whole lines before they go to memory.
+#ifndef TK_SCALE_STORE_POLICY
+#define TK_SCALE_STORE_POLICY 0
+#endif
+__device__ __forceinline__ void store_scale(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, int(byte_off), 0, TK_SCALE_STORE_POLICY);
+}
+
 // ---------------------------------------------------------------------------
 // silu32 table.  silu32(g) = fp32 nearest to g / (1 + e^-g) is needed exactly
 // (correctly rounded) for every bf16 gate.  Outside |g| in [2^-26, 128] it has
@@ -260,7 +271,7 @@ __device__ __forceinline__ void cast_segment(const float (&x)[8], uint32_t amax_
     }
     constexpr int kLanesPerGroup = G / 8;
     if constexpr (SF == kScaleF32) {
-        if ((lane % kLanesPerGroup) == 0) store4(srow, (col / G) * 4, __float_as_uint(s));
+        if ((lane % kLanesPerGroup) == 0) store_scale(srow, (col / G) * 4, __float_as_uint(s));
     } else {
         // Four consecutive groups' exponent bytes -> one little-endian int32,
         // written by the first lane of the first group.
@@ -268,7 +279,7 @@ __device__ __forceinline__ void cast_segment(const float (&x)[8], uint32_t amax_
         const uint32_t b2 = shfl_u32(e8, lane + 2 * kLanesPerGroup);
         const uint32_t b3 = shfl_u32(e8, lane + 3 * kLanesPerGroup);
         if ((lane % (4 * kLanesPerGroup)) == 0)
-            store4(srow, (col / (4 * G)) * 4, e8 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+            store_scale(srow, (col / (4 * G)) * 4, e8 | (b1 << 8) | (b2 << 16) | (b3 << 24));
     }
 }
 
@@ -528,8 +539,24 @@ using KernelFn = void (*)(CastParams);
 // workgroup.  The plain cast runs one unit per wave; the SwiGLU form keeps a
 // bounded grid so that each workgroup's copy of the silu32 table into LDS
 // serves many units.
-constexpr int kCastU = 2, kCastWPB = 2;
-constexpr int kSwigluU = 2, kSwigluWPB = 8, kSwigluBlocksPerCU = 4;
+#ifndef TK_CAST_U
+#define TK_CAST_U 2
+#endif
+#ifndef TK_CAST_WPB
+#define TK_CAST_WPB 2
+#endif
+#ifndef TK_SWIGLU_U
+#define TK_SWIGLU_U 1
+#endif
+#ifndef TK_SWIGLU_WPB
+#define TK_SWIGLU_WPB 16
+#endif
+#ifndef TK_SWIGLU_BLOCKS_PER_CU
+#define TK_SWIGLU_BLOCKS_PER_CU 2
+#endif
+constexpr int kCastU = TK_CAST_U, kCastWPB = TK_CAST_WPB;
+constexpr int kSwigluU = TK_SWIGLU_U, kSwigluWPB = TK_SWIGLU_WPB;
+constexpr int kSwigluBlocksPerCU = TK_SWIGLU_BLOCKS_PER_CU;
 
 // Kernel pointers by [group index][out dtype][variant]; variant 0 = plain
 // fp32 scale, 1 = power-of-two fp32 scale, 2 = power-of-two UE8M0 x4.
