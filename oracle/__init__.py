@@ -67,6 +67,14 @@ def _open(path) -> ctypes.CDLL:
     lib.oracle_group_scale_n.restype = None
     lib.oracle_div_n.argtypes = [p, p, p, i64]
     lib.oracle_div_n.restype = None
+    lib.oracle_per_token_dequant.argtypes = [p, i64, i64, i64, p, i64, i32, i32, i32, p, i64, i32]
+    lib.oracle_per_token_dequant.restype = ctypes.c_int
+    lib.oracle_per_token_cast_back.argtypes = [p, i64, i64, i64, p, i64, i32, i32, i32, p, p, p]
+    lib.oracle_per_token_cast_back.restype = ctypes.c_int
+    lib.oracle_code_value_n.argtypes = [p, p, i64, i32]
+    lib.oracle_code_value_n.restype = None
+    lib.oracle_f32_to_bf16_n.argtypes = [p, p, i64]
+    lib.oracle_f32_to_bf16_n.restype = None
     return lib
 
 
@@ -202,4 +210,54 @@ def divide(x, s) -> np.ndarray:
     s = np.ascontiguousarray(np.broadcast_to(s, x.shape), dtype=np.float32)
     out = np.empty(x.shape, dtype=np.float32)
     _lib().oracle_div_n(_ptr(x), _ptr(s), _ptr(out), x.size)
+    return out
+
+
+def per_token_dequant(q: np.ndarray, scales: np.ndarray, cols: int, group: int = 128,
+                      in_dtype: str = "e4m3", scale_fmt: str = "f32", out: str = "bf16"):
+    """Oracle dequantization: codes + scales -> y = fl32(value(code) * s) as
+    fp32 (out="f32") or bf16 bit patterns (out="bf16"), [rows, cols]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    rows = q.shape[0]
+    sc = np.ascontiguousarray(scales)
+    y = np.zeros((rows, cols), dtype=np.float32 if out == "f32" else np.uint16)
+    rc = _lib().oracle_per_token_dequant(
+        _ptr(q), rows, cols, q.shape[1], _ptr(sc), sc.shape[1], group, _QDTYPES[in_dtype],
+        _SCALE_FMTS[scale_fmt], _ptr(y), cols, int(out == "f32"))
+    if rc != 0:
+        raise ValueError("oracle rejected the dequantization arguments")
+    return y
+
+
+def per_token_cast_back(x: np.ndarray, group: int = 128, out_dtype: str = "e4m3",
+                        round_pow2: bool = False):
+    """Oracle cast-and-cast-back: bf16 bits [rows, cols] -> bf16 bits of the
+    dequantized cast (fp32 scales; UE8M0 packing does not change values)."""
+    _check_2d(x)
+    rows, cols = x.shape
+    y = np.zeros((rows, cols), dtype=np.uint16)
+    work = np.empty(cols, dtype=np.float32)
+    qwork = np.zeros(cols, dtype=np.uint8)
+    swork = np.empty(max(cols // group, 1), dtype=np.float32)
+    rc = _lib().oracle_per_token_cast_back(
+        _ptr(x), rows, cols, x.strides[0] // 2, _ptr(y), cols, group, _QDTYPES[out_dtype],
+        int(bool(round_pow2)), _ptr(work), _ptr(qwork), _ptr(swork))
+    if rc != 0:
+        raise ValueError("oracle rejected the cast-back arguments")
+    return y
+
+
+def code_value(codes, in_dtype: str = "e4m3") -> np.ndarray:
+    """fp32 value of E4M3 bytes or E2M1 nibbles, elementwise."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float32)
+    _lib().oracle_code_value_n(_ptr(c), _ptr(out), c.size, _QDTYPES[in_dtype])
+    return out
+
+
+def f32_to_bf16(v) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, nearest with ties to even, elementwise."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _lib().oracle_f32_to_bf16_n(_ptr(v), _ptr(out), v.size)
     return out

@@ -32,6 +32,11 @@
  *      code, keeping the sign (also of zero);
  *   7. SwiGLU form: x_i is replaced by h_i = fl32(silu32(g_i) * u_i), where
  *      silu32(g) is the fp32 value nearest to g / (1 + e^-g).
+ * Dequantization ("Tile Kernels" (PyPI, v2.0.0), Features: "casting and
+ * dequantization") maps a code back to y = fl32(value(code) * s), returned as
+ * fp32 or rounded to bf16 (nearest, ties to even); the per-token
+ * cast-and-cast-back ("TileKernels" (aiwiki.ai), Version 2.0.0) is the cast
+ * above followed by that dequantization, bf16 out.
  * Every float operation below is one IEEE binary32 operation rounded to
  * nearest-even; build with -O2 -ffp-contract=off and without fast-math.
  * Results for NaN or Inf inputs are outside the contract.
@@ -252,6 +257,80 @@ int oracle_swiglu_per_token_cast(const uint16_t *gate_up, int64_t rows, int64_t 
     return 0;
 }
 
+/* ---- dequantization and cast-back ------------------------------------ */
+
+/* fp32 -> bf16 bit pattern, round to nearest, ties to even (finite inputs
+ * and infinities; NaN is outside the contract). */
+static uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t b = bits_from_f32(f);
+    uint32_t lsb = (b >> 16) & 1u;
+    return (uint16_t)((b + 0x7FFFu + lsb) >> 16);
+}
+
+/* Value of a code: E4M3 byte, or E2M1 nibble (low 4 bits). */
+static float code_value(int32_t qdtype, uint8_t code)
+{
+    if (qdtype == ORACLE_E4M3) {
+        double m = g_e4m3[code & 0x7F];       /* 0x7F (NaN) is never produced */
+        return (float)((code & 0x80) ? -m : m);
+    }
+    double m = g_e2m1[code & 0x7];
+    return (float)((code & 0x8) ? -m : m);
+}
+
+/* q: codes [rows, cols] (E4M3) or [rows, cols/2] (E2M1), row stride q_ld
+ * bytes; scales as produced by the cast (fp32 or UE8M0 x4 int32, row stride
+ * s_ld elements); y: fp32 (y_f32 != 0) or bf16 bits [rows, cols], row stride
+ * y_ld elements.  y = fl32(value(code) * s), then bf16 RNE when asked. */
+int oracle_per_token_dequant(const uint8_t *q, int64_t rows, int64_t cols, int64_t q_ld,
+                             const void *scales, int64_t s_ld, int32_t group, int32_t qdtype,
+                             int32_t scale_fmt, void *y, int64_t y_ld, int32_t y_f32)
+{
+    if (!valid_common(rows, cols, group, qdtype, scale_fmt == ORACLE_SCALE_UE8M0_X4, scale_fmt)) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) {
+            int64_t j = c / group;
+            float s;
+            if (scale_fmt == ORACLE_SCALE_F32) {
+                s = ((const float *)scales)[r * s_ld + j];
+            } else {
+                uint32_t dw = ((const uint32_t *)scales)[r * s_ld + j / 4];
+                uint32_t e = (dw >> (8 * (j % 4))) & 0xFF;
+                s = f32_from_bits(e << 23);    /* 2^(e - 127); e in [1, 254] */
+            }
+            uint8_t code;
+            if (qdtype == ORACLE_E4M3) {
+                code = q[r * q_ld + c];
+            } else {
+                uint8_t byte = q[r * q_ld + c / 2];
+                code = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+            }
+            float v = code_value(qdtype, code) * s;
+            if (y_f32) ((float *)y)[r * y_ld + c] = v;
+            else ((uint16_t *)y)[r * y_ld + c] = f32_to_bf16_rne(v);
+        }
+    }
+    return 0;
+}
+
+/* Cast then dequantize, bf16 out: y [rows, cols] bf16 bits, row stride y_ld. */
+int oracle_per_token_cast_back(const uint16_t *x, int64_t rows, int64_t cols, int64_t x_ld,
+                               uint16_t *y, int64_t y_ld, int32_t group, int32_t qdtype,
+                               int32_t round_pow2, float *work /* cols floats */,
+                               uint8_t *qwork /* cols bytes */, float *swork /* cols/group floats */)
+{
+    if (!valid_common(rows, cols, group, qdtype, round_pow2, ORACLE_SCALE_F32)) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) work[c] = bf16_to_f32(x[r * x_ld + c]);
+        cast_row(work, cols, qwork, swork, group, qdtype, round_pow2, ORACLE_SCALE_F32);
+        if (oracle_per_token_dequant(qwork, 1, cols, cols, swork, cols / group, group, qdtype,
+                                     ORACLE_SCALE_F32, y + r * y_ld, y_ld, 0) != 0)
+            return -1;
+    }
+    return 0;
+}
+
 /* ---- array forms of the single steps, for the pin tests -------------- */
 
 void oracle_encode_e4m3_n(const float *v, uint8_t *out, int64_t n)
@@ -273,6 +352,16 @@ void oracle_group_scale_n(const float *amax, float *s, uint8_t *e8, int64_t n, i
                           int32_t round_pow2)
 {
     for (int64_t i = 0; i < n; ++i) s[i] = oracle_group_scale(amax[i], qdtype, round_pow2, &e8[i]);
+}
+
+void oracle_code_value_n(const uint8_t *codes, float *out, int64_t n, int32_t qdtype)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = code_value(qdtype, codes[i]);
+}
+
+void oracle_f32_to_bf16_n(const float *v, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne(v[i]);
 }
 
 /* Step 6's division, elementwise: out[i] = x[i] / s[i]. */

@@ -137,3 +137,34 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
 def decode_e2m1_nibbles(n: np.ndarray) -> np.ndarray:
     mag = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float32)[n & 7]
     return np.where(n & 8, -mag, mag).astype(np.float32)
+
+
+def f32_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """torch's fp32 -> bf16 cast (nearest, ties to even) as uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def per_token_dequant(q, scales, cols, group, in_dtype, scale_fmt, out="bf16"):
+    """Codes + scales -> fl32(value * s) (torch float8 decode / the E2M1 table,
+    numpy fp32 multiply), then torch's bf16 cast when out == "bf16"."""
+    rows = q.shape[0]
+    if in_dtype == "e4m3":
+        val = decode_e4m3(q)
+    else:
+        n = np.empty((rows, cols), dtype=np.uint8)
+        n[:, 0::2] = q & 0xF
+        n[:, 1::2] = q >> 4
+        val = decode_e2m1_nibbles(n)
+    if scale_fmt == "f32":
+        s = np.asarray(scales, dtype=np.float32)
+    else:
+        e = np.ascontiguousarray(scales).view(np.uint8).reshape(rows, cols // group).astype(np.int32)
+        s = np.ldexp(np.float32(1.0), e - 127).astype(np.float32)
+    y = (val * np.repeat(s, group, axis=1)).astype(np.float32)
+    return y if out == "f32" else f32_to_bf16_bits(y)
+
+
+def per_token_cast_back(x_bits, group, out_dtype, round_pow2):
+    q, s = per_token_cast(x_bits, group, out_dtype, round_pow2, "f32")
+    return per_token_dequant(q, s, x_bits.shape[1], group, out_dtype, "f32", "bf16")

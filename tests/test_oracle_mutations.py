@@ -13,6 +13,7 @@ import pathlib
 import pytest
 
 import oracle
+import test_oracle_dequant_pins as dpins
 import test_oracle_pins as pins
 
 SRC = pathlib.Path(oracle.__file__).resolve().parent / "tk_oracle.c"
@@ -42,23 +43,35 @@ MUTATIONS = [
      "float u = bf16_to_f32(row[c]);\n            float g = bf16_to_f32(row[cols + c]);", None),
     ("group offset off by one group", "const float *x = v + j * group;",
      "const float *x = v + ((j + 1) % ngroups) * group;", None),
+    ("bf16 truncation", "return (uint16_t)((b + 0x7FFFu + lsb) >> 16);", "(void)lsb; return (uint16_t)(b >> 16);", None),
+    ("bf16 ties away", "return (uint16_t)((b + 0x7FFFu + lsb) >> 16);", "(void)lsb; return (uint16_t)((b + 0x8000u) >> 16);", None),
+    ("dequant UE8M0 exponent off by one", "s = f32_from_bits(e << 23);", "s = f32_from_bits((e + 1) << 23);", None),
+    ("dequant nibbles swapped", "code = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);",
+     "code = (c % 2 == 1) ? (byte & 0xF) : (byte >> 4);", None),
+    ("decode drops the sign", "return (float)((code & 0x80) ? -m : m);", "return (float)m;", None),
 ]
 
 
 def _checks():
+    """Cheap, broad checks first; each mutant stops at the first failing one."""
     gold = pins._golden()
     out = [lambda c=c: pins.test_hand_examples(c) for c in gold["cases"]]
     out += [pins.test_e4m3_tie_table, pins.test_e2m1_tie_table, pins.test_floor_constant_bits,
+            dpins.test_e4m3_code_values_vs_torch, dpins.test_e2m1_code_values_by_hand,
+            dpins.test_bf16_rounding_vs_torch,
+            lambda: dpins.test_dequant_vs_library_composition(32, "e2m1", "ue8m0", True, "bf16"),
+            lambda: dpins.test_dequant_vs_library_composition(128, "e4m3", "f32", False, "f32"),
+            lambda: dpins.test_cast_back_vs_library_composition(64, "e4m3", True),
+            lambda: pins.test_whole_tensor_vs_library_composition(32, "e2m1", True, "ue8m0", 3, 4),
+            lambda: pins.test_whole_tensor_division_hard_cases("e4m3"),
             pins.test_e4m3_exhaustive_bf16_times_pow2_vs_torch,
             pins.test_e2m1_exhaustive_bf16_times_pow2_vs_quantum_rounding,
             lambda: pins.test_scale_division_exact_all_bf16_amax("e4m3", 448),
             lambda: pins.test_scale_division_exact_all_bf16_amax("e2m1", 6),
-            lambda: pins.test_pow2_round_up_exact("e4m3", 448),
             pins.test_division_vs_exact_and_numpy,
-            lambda: pins.test_whole_tensor_division_hard_cases("e4m3"),
-            pins.test_silu32_every_bf16_gate_vs_60_digit_decimal,
             pins.test_swiglu_sweep_vs_library_composition,
-            lambda: pins.test_whole_tensor_vs_library_composition(32, "e2m1", True, "ue8m0", 3, 4)]
+            pins.test_silu32_every_bf16_gate_vs_60_digit_decimal,
+            lambda: pins.test_pow2_round_up_exact("e4m3", 448)]
     return out
 
 
