@@ -7,17 +7,22 @@ the library with ``python -m activation_quantization_token_amd.build``.
 from .binding import (  # noqa: F401
     GROUPS,
     QDTYPES,
+    OUT_DTYPES,
     SCALE_FMTS,
     TkError,
     copy_stream,
     empty_outputs,
     load_library,
     per_token_cast,
+    per_token_cast_back,
+    per_token_dequant,
     silu32_bf16,
     swiglu_per_token_cast,
     tk_abi_version,
     tk_copy_stream,
     tk_per_token_cast,
+    tk_per_token_cast_back,
+    tk_per_token_dequant,
     tk_prepare_device,
     tk_silu32_bf16,
     tk_status_string,

@@ -22,6 +22,7 @@ LIB_PATH = _PKG / "libtk_quant.so"
 TK_SUCCESS = 0
 QDTYPES = {"e4m3": 0, "e2m1": 1}
 SCALE_FMTS = {"f32": 0, "ue8m0": 1}
+OUT_DTYPES = {"bf16": 0, "f32": 1}
 GROUPS = (16, 32, 64, 128)
 
 _lock = threading.Lock()
@@ -52,6 +53,10 @@ def load_library(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, i32, i32, i32, i32, vp]
             fn.restype = ctypes.c_int
+        lib.tk_per_token_dequant.argtypes = [vp, i64, i64, i64, vp, i64, i32, i32, i32, vp, i64, i32, vp]
+        lib.tk_per_token_dequant.restype = ctypes.c_int
+        lib.tk_per_token_cast_back.argtypes = [vp, i64, i64, i64, vp, i64, i32, i32, i32, vp]
+        lib.tk_per_token_cast_back.restype = ctypes.c_int
         lib.tk_silu32_bf16.argtypes = [vp, vp, i64, vp]
         lib.tk_silu32_bf16.restype = ctypes.c_int
         lib.tk_copy_stream.argtypes = [vp, vp, i64, vp]
@@ -198,3 +203,52 @@ def swiglu_per_token_cast(gate_up: torch.Tensor, group: int = 128, out_dtype: st
         raise ValueError("gate_up must have an even number of columns")
     return _run(tk_swiglu_per_token_cast, gate_up, gate_up.shape[1] // 2, group, out_dtype,
                 round_pow2, scale_fmt, out, stream)
+
+
+def tk_per_token_dequant(q: int, rows: int, cols: int, q_ld: int, scales: int, s_ld: int, group: int,
+                         in_dtype: int, scale_fmt: int, y: int, y_ld: int, y_dtype: int,
+                         stream: int) -> int:
+    """Raw C call with integer pointers; returns the tk_status code."""
+    return load_library().tk_per_token_dequant(q, rows, cols, q_ld, scales, s_ld, group, in_dtype,
+                                               scale_fmt, y, y_ld, y_dtype, stream)
+
+
+def tk_per_token_cast_back(x: int, rows: int, cols: int, x_ld: int, y: int, y_ld: int, group: int,
+                           out_dtype: int, round_pow2: int, stream: int) -> int:
+    """Raw C call with integer pointers; returns the tk_status code."""
+    return load_library().tk_per_token_cast_back(x, rows, cols, x_ld, y, y_ld, group, out_dtype,
+                                                 round_pow2, stream)
+
+
+def per_token_dequant(q: torch.Tensor, scales: torch.Tensor, cols: int, group: int = 128,
+                      in_dtype: str = "e4m3", scale_fmt: str = "f32", out_dtype: str = "bf16",
+                      out=None, stream=None) -> torch.Tensor:
+    """Codes + scales (as per_token_cast returns them) -> y [rows, cols] in
+    bf16 or fp32, y = value(code) * s."""
+    for t, what in ((q, "q"), (scales, "scales")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+            raise TypeError(f"{what} must be a 2-D row-contiguous GPU tensor")
+    if q.dtype != torch.uint8:
+        raise TypeError("q must be uint8")
+    rows = q.shape[0]
+    ydt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    y = torch.empty((rows, cols), dtype=ydt, device=q.device) if out is None else out
+    if y.dtype != ydt or y.dim() != 2 or y.stride(1) != 1 or y.shape[0] != rows or y.device != q.device:
+        raise ValueError("out must be a row-contiguous tensor of the output dtype on q's device")
+    _check(tk_per_token_dequant(q.data_ptr(), rows, cols, q.stride(0), scales.data_ptr(), scales.stride(0),
+                                group, QDTYPES[in_dtype], SCALE_FMTS[scale_fmt], y.data_ptr(), y.stride(0),
+                                OUT_DTYPES[out_dtype], _stream_handle(stream, q.device)))
+    return y
+
+
+def per_token_cast_back(x: torch.Tensor, group: int = 128, out_dtype: str = "e4m3",
+                        round_pow2: bool = False, out=None, stream=None) -> torch.Tensor:
+    """bf16 x -> bf16 dequantized per-token cast of x, fused (no codes written)."""
+    _check_input(x, "x")
+    rows, cols = x.shape
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device) if out is None else out
+    if y.dtype != torch.bfloat16 or y.dim() != 2 or y.stride(1) != 1 or tuple(y.shape) != (rows, cols):
+        raise ValueError("out must be a row-contiguous bf16 tensor of x's shape")
+    _check(tk_per_token_cast_back(x.data_ptr(), rows, cols, x.stride(0), y.data_ptr(), y.stride(0), group,
+                                  QDTYPES[out_dtype], int(bool(round_pow2)), _stream_handle(stream, x.device)))
+    return y

@@ -203,8 +203,9 @@ __device__ float silu32_exact(uint32_t b, const float *tab)
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_mov(uint32_t v)
 {
-    // Every DPP pattern used here reads a lane inside the same 16-lane row, so
-    // all lanes are written (row and bank masks full).
+    // Row and bank masks full.  Lanes whose source falls outside their
+    // 16-lane row (row_shl near the row end) keep 0; no result of such a lane
+    // is used.
     return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
 }
 
@@ -228,11 +229,16 @@ __device__ __forceinline__ uint32_t shfl_u32(uint32_t v, int src_lane)
 
 // ---------------------------------------------------------------------------
 // The per-segment cast: 8 fp32 values per lane (columns col .. col+7 of one
-// row), their |max| bits, and buffer descriptors of the row's codes and scales.
+// row) and their |max| bits -> codes in registers plus the group's scale.
 
-template <int G, int QD, bool POW2, int SF>
-__device__ __forceinline__ void cast_segment(const float (&x)[8], uint32_t amax_bits, int lane, uint32_t col,
-                                             __amdgpu_buffer_rsrc_t qrow, __amdgpu_buffer_rsrc_t srow)
+struct Quantized {
+    u32x2 codes;    // E4M3: 8 bytes; E2M1: 8 nibbles in codes.x
+    float s;        // the group's scale
+    uint32_t e8;    // its biased exponent byte (power-of-two scales)
+};
+
+template <int G, int QD, bool POW2>
+__device__ __forceinline__ Quantized quantize_segment(const float (&x)[8], uint32_t amax_bits)
 {
     constexpr float D = (QD == kE4M3) ? 448.0f : 6.0f;
     amax_bits = group_max<G>(amax_bits);
@@ -256,31 +262,103 @@ __device__ __forceinline__ void cast_segment(const float (&x)[8], uint32_t amax_
         v[i] = POW2 ? x[i] * inv : x[i] / s;
         v[i] = __builtin_amdgcn_fmed3f(v[i], D, -D);
     }
+    Quantized out;
+    out.s = s;
+    out.e8 = e8;
     if constexpr (QD == kE4M3) {
         uint32_t lo = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false));
         lo = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], int(lo), true));
         uint32_t hi = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false));
         hi = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], int(hi), true));
-        store8(qrow, col, u32x2{lo, hi});
+        out.codes = u32x2{lo, hi};
     } else {
         uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], 1.0f, 1);
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], 1.0f, 2);
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], 1.0f, 3);
-        store4(qrow, col / 2, r);
+        out.codes = u32x2{r, 0u};
     }
+    return out;
+}
+
+// Codes and scales of one segment to the row's buffers.
+template <int G, int QD, int SF>
+__device__ __forceinline__ void store_segment(const Quantized &qz, int lane, uint32_t col,
+                                              __amdgpu_buffer_rsrc_t qrow, __amdgpu_buffer_rsrc_t srow)
+{
+    if constexpr (QD == kE4M3) store8(qrow, col, qz.codes);
+    else store4(qrow, col / 2, qz.codes.x);
     constexpr int kLanesPerGroup = G / 8;
     if constexpr (SF == kScaleF32) {
-        if ((lane % kLanesPerGroup) == 0) store_scale(srow, (col / G) * 4, __float_as_uint(s));
+        if ((lane % kLanesPerGroup) == 0) store_scale(srow, (col / G) * 4, __float_as_uint(qz.s));
     } else {
         // Four consecutive groups' exponent bytes -> one little-endian int32,
-        // written by the first lane of the first group.
-        const uint32_t b1 = shfl_u32(e8, lane + kLanesPerGroup);
-        const uint32_t b2 = shfl_u32(e8, lane + 2 * kLanesPerGroup);
-        const uint32_t b3 = shfl_u32(e8, lane + 3 * kLanesPerGroup);
+        // written by the first lane of the first group.  For G <= 32 the four
+        // groups lie in one 16-lane DPP row and row_shl moves (lane i reads
+        // lane i + N) gather them without an LDS round trip.
+        uint32_t b1, b2, b3;
+        if constexpr (G <= 32) {
+            b1 = dpp_mov<0x100 + kLanesPerGroup>(qz.e8);
+            b2 = dpp_mov<0x100 + 2 * kLanesPerGroup>(qz.e8);
+            b3 = dpp_mov<0x100 + 3 * kLanesPerGroup>(qz.e8);
+        } else {
+            b1 = shfl_u32(qz.e8, lane + kLanesPerGroup);
+            b2 = shfl_u32(qz.e8, lane + 2 * kLanesPerGroup);
+            b3 = shfl_u32(qz.e8, lane + 3 * kLanesPerGroup);
+        }
         if ((lane % (4 * kLanesPerGroup)) == 0)
-            store_scale(srow, (col / (4 * G)) * 4, e8 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+            store_scale(srow, (col / (4 * G)) * 4, qz.e8 | (b1 << 8) | (b2 << 16) | (b3 << 24));
     }
+}
+
+template <int G, int QD, bool POW2, int SF>
+__device__ __forceinline__ void cast_segment(const float (&x)[8], uint32_t amax_bits, int lane, uint32_t col,
+                                             __amdgpu_buffer_rsrc_t qrow, __amdgpu_buffer_rsrc_t srow)
+{
+    store_segment<G, QD, SF>(quantize_segment<G, QD, POW2>(x, amax_bits), lane, col, qrow, srow);
+}
+
+// Code values back to fp32 (exact) with the hardware decoders, times s.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int QD>
+__device__ __forceinline__ void dequant_codes(u32x2 codes, float s, float (&y)[8])
+{
+    f32x2 d[4];
+    if constexpr (QD == kE4M3) {
+        d[0] = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes.x), false);
+        d[1] = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes.x), true);
+        d[2] = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes.y), false);
+        d[3] = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes.y), true);
+    } else {
+        d[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, 1.0f, 0);
+        d[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, 1.0f, 1);
+        d[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, 1.0f, 2);
+        d[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, 1.0f, 3);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        y[2 * k] = d[k].x * s;
+        y[2 * k + 1] = d[k].y * s;
+    }
+}
+
+// 8 fp32 -> 8 bf16 (nearest, ties to even; v_cvt_pk_bf16_f32) in 16 bytes.
+__device__ __forceinline__ u32x4 pack_bf16x8(const float (&y)[8])
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    u32x4 out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const bf16x2 p = {__bf16(y[2 * k]), __bf16(y[2 * k + 1])};
+        out[k] = __builtin_bit_cast(uint32_t, p);
+    }
+    return out;
+}
+
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, int(byte_off), 0, kNonTemporal);
 }
 
 __device__ __forceinline__ void widen8(const u32x4 &w, float (&x)[8])
@@ -373,6 +451,162 @@ __global__ __launch_bounds__(kWave * WPB) void cast_kernel(CastParams p)
             float x[8];
             widen8(w[k], x);
             cast_segment<G, QD, POW2, SF>(x, amax_bits_bf16x8(w[k]), lane, un.col0 + k * kSegCols, qrow, srow);
+        }
+    }
+}
+
+// Row-per-workgroup form of the cast.  The scale stores of the unit form are
+// many small partial-line writes (one per 512-column segment); here every
+// wave of the workgroup puts its scales into LDS and the row's scales leave in
+// one coalesced store per 256 bytes after a barrier.  Workgroups take rows in
+// order (grid-stride), so the resident rows still form one compact window.
+// Wave w of the W in the workgroup converts runs w, w + W, ... of the row.
+template <int G, int QD, bool POW2, int SF, int U>
+__global__ __launch_bounds__(1024) void cast_rows_kernel(CastParams p)
+{
+    extern __shared__ uint32_t row_scales[];     // the row's scale words
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = int(blockDim.x) >> 6;
+    const uint32_t cols = uint32_t(p.cols);
+    const int runs = int((cols + U * kSegCols - 1) / (U * kSegCols));
+    const uint32_t s_words = SF == kScaleF32 ? cols / G : cols / G / 4;
+    constexpr int kLanesPerGroup = G / 8;
+    for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
+        const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + row * p.x_ld, cols * 2u);
+        __amdgpu_buffer_rsrc_t qrow, srow;
+        output_rows<G, QD, SF>(p, row, qrow, srow);
+        for (int run = wave; run < runs; run += nw) {
+            const uint32_t col0 = uint32_t(run) * uint32_t(U * kSegCols) + uint32_t(lane) * 8u;
+            u32x4 w[U];
+#pragma unroll
+            for (int k = 0; k < U; ++k) w[k] = load16(xrow, (col0 + k * kSegCols) * 2u);
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const uint32_t col = col0 + k * kSegCols;
+                float x[8];
+                widen8(w[k], x);
+                const Quantized qz = quantize_segment<G, QD, POW2>(x, amax_bits_bf16x8(w[k]));
+                if constexpr (QD == kE4M3) store8(qrow, col, qz.codes);
+                else store4(qrow, col / 2, qz.codes.x);
+                if constexpr (SF == kScaleF32) {
+                    if ((lane % kLanesPerGroup) == 0 && col < cols) row_scales[col / G] = __float_as_uint(qz.s);
+                } else {
+                    uint32_t b1, b2, b3;
+                    if constexpr (G <= 32) {
+                        b1 = dpp_mov<0x100 + kLanesPerGroup>(qz.e8);
+                        b2 = dpp_mov<0x100 + 2 * kLanesPerGroup>(qz.e8);
+                        b3 = dpp_mov<0x100 + 3 * kLanesPerGroup>(qz.e8);
+                    } else {
+                        b1 = shfl_u32(qz.e8, lane + kLanesPerGroup);
+                        b2 = shfl_u32(qz.e8, lane + 2 * kLanesPerGroup);
+                        b3 = shfl_u32(qz.e8, lane + 3 * kLanesPerGroup);
+                    }
+                    if ((lane % (4 * kLanesPerGroup)) == 0 && col < cols)
+                        row_scales[col / (4 * G)] = qz.e8 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+                }
+            }
+        }
+        __syncthreads();
+        for (uint32_t t = threadIdx.x; t < s_words; t += blockDim.x) store_scale(srow, t * 4u, row_scales[t]);
+        __syncthreads();                         // the next row reuses row_scales
+    }
+}
+
+// Fused cast-and-cast-back: the cast's codes and scales stay in registers and
+// are decoded straight back to bf16.
+struct BackParams {
+    const uint16_t *x;
+    int64_t rows, cols, x_ld;
+    uint16_t *y;         // bf16 bits
+    int64_t y_ld;
+};
+
+template <int G, int QD, bool POW2, int U, int WPB>
+__global__ __launch_bounds__(kWave * WPB) void cast_back_kernel(BackParams p)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = int64_t(blockIdx.x) * WPB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = int64_t(gridDim.x) * WPB;
+    const int64_t nseg = (p.cols + kSegCols - 1) / kSegCols;
+    const int64_t runs = (nseg + U - 1) / U;
+    const int64_t units = p.rows * runs;
+    const uint32_t row_bytes = uint32_t(p.cols) * 2u;
+    for (int64_t unit = wave; unit < units; unit += nwaves) {
+        const Unit un = decode_unit<U>(unit, runs, lane);
+        const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + un.row * p.x_ld, row_bytes);
+        const __amdgpu_buffer_rsrc_t yrow = row_buffer(p.y + un.row * p.y_ld, row_bytes);
+        u32x4 w[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) w[k] = load16(xrow, (un.col0 + k * kSegCols) * 2u);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            float x[8], y[8];
+            widen8(w[k], x);
+            const Quantized qz = quantize_segment<G, QD, POW2>(x, amax_bits_bf16x8(w[k]));
+            dequant_codes<QD>(qz.codes, qz.s, y);
+            store16(yrow, (un.col0 + k * kSegCols) * 2u, pack_bf16x8(y));
+        }
+    }
+}
+
+// Dequantization: codes + scales -> y = fl32(value * s), bf16 or fp32.
+struct DequantParams {
+    const uint8_t *q;
+    int64_t rows, cols, q_ld;
+    const void *s;
+    int64_t s_ld;
+    void *y;
+    int64_t y_ld;        // elements of y's type
+};
+
+template <int G, int QD, int SF, bool OUT_F32, int U, int WPB>
+__global__ __launch_bounds__(kWave * WPB) void dequant_kernel(DequantParams p)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = int64_t(blockIdx.x) * WPB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = int64_t(gridDim.x) * WPB;
+    const int64_t nseg = (p.cols + kSegCols - 1) / kSegCols;
+    const int64_t runs = (nseg + U - 1) / U;
+    const int64_t units = p.rows * runs;
+    const uint32_t cols = uint32_t(p.cols);
+    for (int64_t unit = wave; unit < units; unit += nwaves) {
+        const Unit un = decode_unit<U>(unit, runs, lane);
+        const __amdgpu_buffer_rsrc_t qrow = row_buffer(p.q + un.row * p.q_ld, QD == kE4M3 ? cols : cols / 2);
+        const __amdgpu_buffer_rsrc_t srow =
+            SF == kScaleF32 ? row_buffer(static_cast<const float *>(p.s) + un.row * p.s_ld, (cols / G) * 4u)
+                            : row_buffer(static_cast<const uint32_t *>(p.s) + un.row * p.s_ld, cols / G);
+        const __amdgpu_buffer_rsrc_t yrow =
+            OUT_F32 ? row_buffer(static_cast<float *>(p.y) + un.row * p.y_ld, cols * 4u)
+                    : row_buffer(static_cast<uint16_t *>(p.y) + un.row * p.y_ld, cols * 2u);
+        u32x2 codes[U];
+        uint32_t sw[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t col = un.col0 + k * kSegCols;
+            if constexpr (QD == kE4M3)
+                codes[k] = __builtin_amdgcn_raw_buffer_load_b64(qrow, int(col), 0, kNonTemporal);
+            else
+                codes[k] = u32x2{__builtin_amdgcn_raw_buffer_load_b32(qrow, int(col / 2), 0, kNonTemporal), 0u};
+            sw[k] = SF == kScaleF32 ? __builtin_amdgcn_raw_buffer_load_b32(srow, int((col / G) * 4), 0, 0)
+                                    : __builtin_amdgcn_raw_buffer_load_b32(srow, int((col / (4 * G)) * 4), 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t col = un.col0 + k * kSegCols;
+            float sc;
+            if constexpr (SF == kScaleF32) sc = __uint_as_float(sw[k]);
+            else sc = __uint_as_float(((sw[k] >> (8 * ((col / G) % 4))) & 0xFFu) << 23);   // 2^(byte-127)
+            float y[8];
+            dequant_codes<QD>(codes[k], sc, y);
+            if constexpr (OUT_F32) {
+                store16(yrow, col * 4u, u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                                               __float_as_uint(y[3])});
+                store16(yrow, col * 4u + 16u, u32x4{__float_as_uint(y[4]), __float_as_uint(y[5]),
+                                                     __float_as_uint(y[6]), __float_as_uint(y[7])});
+            } else {
+                store16(yrow, col * 2u, pack_bf16x8(y));
+            }
         }
     }
 }
@@ -558,6 +792,36 @@ constexpr int kCastU = TK_CAST_U, kCastWPB = TK_CAST_WPB;
 constexpr int kSwigluU = TK_SWIGLU_U, kSwigluWPB = TK_SWIGLU_WPB;
 constexpr int kSwigluBlocksPerCU = TK_SWIGLU_BLOCKS_PER_CU;
 
+#ifndef TK_CAST_ROWS
+#define TK_CAST_ROWS 1
+#endif
+constexpr bool kCastRows = TK_CAST_ROWS != 0;
+constexpr int64_t kRowScaleLdsBytes = 32768;   // rows with more scale bytes use the unit form
+constexpr int kRowMaxWaves = 16;
+
+using CastFn = void (*)(CastParams);
+struct RowTable {
+    CastFn fn[4][2][3];
+};
+
+template <int G, int QD>
+void fill_rows(CastFn (&t)[3])
+{
+    t[0] = cast_rows_kernel<G, QD, false, kScaleF32, kCastU>;
+    t[1] = cast_rows_kernel<G, QD, true, kScaleF32, kCastU>;
+    t[2] = cast_rows_kernel<G, QD, true, kScaleUE8M0, kCastU>;
+}
+
+RowTable make_row_table()
+{
+    RowTable t;
+    fill_rows<16, kE4M3>(t.fn[0][0]);  fill_rows<16, kE2M1>(t.fn[0][1]);
+    fill_rows<32, kE4M3>(t.fn[1][0]);  fill_rows<32, kE2M1>(t.fn[1][1]);
+    fill_rows<64, kE4M3>(t.fn[2][0]);  fill_rows<64, kE2M1>(t.fn[2][1]);
+    fill_rows<128, kE4M3>(t.fn[3][0]); fill_rows<128, kE2M1>(t.fn[3][1]);
+    return t;
+}
+
 // Kernel pointers by [group index][out dtype][variant]; variant 0 = plain
 // fp32 scale, 1 = power-of-two fp32 scale, 2 = power-of-two UE8M0 x4.
 struct KernelTable {
@@ -616,6 +880,21 @@ tk_status launch(bool swiglu, const void *x, int64_t rows, int64_t cols, int64_t
     static const KernelTable cast_table = make_table<false>();
     static const KernelTable swiglu_table = make_table<true>();
     const int variant = !round_pow2 ? 0 : (scale_fmt == kScaleF32 ? 1 : 2);
+    const int64_t s_words = scale_fmt == kScaleF32 ? cols / group : cols / group / 4;
+    if (!swiglu && kCastRows && s_words * 4 <= kRowScaleLdsBytes) {
+        static const RowTable row_table = make_row_table();
+        const int64_t runs = (cols + kCastU * kSegCols - 1) / (kCastU * kSegCols);
+        const int waves = int(runs < kRowMaxWaves ? runs : kRowMaxWaves);
+        int64_t blocks = rows < int64_t(0x7FFFFFFF) ? rows : int64_t(0x7FFFFFFF);
+        CastParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld,
+                     scales, s_ld};
+        void *args[] = {&p};
+        const CastFn fn = row_table.fn[group_index(group)][out_dtype][variant];
+        if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * waves), args,
+                            size_t(s_words * 4), s) != hipSuccess)
+            return TK_ERROR_LAUNCH;
+        return TK_SUCCESS;
+    }
     const KernelFn fn = (swiglu ? swiglu_table : cast_table).fn[group_index(group)][out_dtype][variant];
     const int U = swiglu ? kSwigluU : kCastU;
     const int wpb = swiglu ? kSwigluWPB : kCastWPB;
@@ -629,6 +908,67 @@ tk_status launch(bool swiglu, const void *x, int64_t rows, int64_t cols, int64_t
     void *args[] = {&p};
     if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * wpb), args,
                         0, s) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    return TK_SUCCESS;
+}
+
+// Cast-and-cast-back and dequantization run the plain cast's launch shape.
+using BackFn = void (*)(BackParams);
+using DequantFn = void (*)(DequantParams);
+
+struct BackTable {
+    BackFn fn[4][2][2];          // [group][code format][pow2]
+};
+struct DequantTable {
+    DequantFn fn[4][2][2][2];    // [group][code format][scale format][fp32 out]
+};
+
+template <int G, int QD>
+void fill_back(BackFn (&t)[2])
+{
+    t[0] = cast_back_kernel<G, QD, false, kCastU, kCastWPB>;
+    t[1] = cast_back_kernel<G, QD, true, kCastU, kCastWPB>;
+}
+
+template <int G, int QD>
+void fill_dequant(DequantFn (&t)[2][2])
+{
+    t[0][0] = dequant_kernel<G, QD, kScaleF32, false, kCastU, kCastWPB>;
+    t[0][1] = dequant_kernel<G, QD, kScaleF32, true, kCastU, kCastWPB>;
+    t[1][0] = dequant_kernel<G, QD, kScaleUE8M0, false, kCastU, kCastWPB>;
+    t[1][1] = dequant_kernel<G, QD, kScaleUE8M0, true, kCastU, kCastWPB>;
+}
+
+BackTable make_back_table()
+{
+    BackTable t;
+    fill_back<16, kE4M3>(t.fn[0][0]);  fill_back<16, kE2M1>(t.fn[0][1]);
+    fill_back<32, kE4M3>(t.fn[1][0]);  fill_back<32, kE2M1>(t.fn[1][1]);
+    fill_back<64, kE4M3>(t.fn[2][0]);  fill_back<64, kE2M1>(t.fn[2][1]);
+    fill_back<128, kE4M3>(t.fn[3][0]); fill_back<128, kE2M1>(t.fn[3][1]);
+    return t;
+}
+
+DequantTable make_dequant_table()
+{
+    DequantTable t;
+    fill_dequant<16, kE4M3>(t.fn[0][0]);  fill_dequant<16, kE2M1>(t.fn[0][1]);
+    fill_dequant<32, kE4M3>(t.fn[1][0]);  fill_dequant<32, kE2M1>(t.fn[1][1]);
+    fill_dequant<64, kE4M3>(t.fn[2][0]);  fill_dequant<64, kE2M1>(t.fn[2][1]);
+    fill_dequant<128, kE4M3>(t.fn[3][0]); fill_dequant<128, kE2M1>(t.fn[3][1]);
+    return t;
+}
+
+bool valid_group(int32_t g) { return g == 16 || g == 32 || g == 64 || g == 128; }
+
+tk_status launch_unit_grid(const void *fn, int64_t rows, int64_t cols, void *params, hipStream_t s)
+{
+    const int64_t nseg = (cols + kSegCols - 1) / kSegCols;
+    const int64_t units = rows * ((nseg + kCastU - 1) / kCastU);
+    int64_t blocks = (units + kCastWPB - 1) / kCastWPB;
+    if (blocks > int64_t(0x7FFFFFFF)) blocks = 0x7FFFFFFF;   // the kernels loop over the rest
+    void *args[] = {params};
+    if (hipLaunchKernel(fn, dim3(uint32_t(blocks)), dim3(kWave * kCastWPB), args, 0, s) != hipSuccess)
         return TK_ERROR_LAUNCH;
     return TK_SUCCESS;
 }
@@ -652,6 +992,58 @@ tk_status tk_swiglu_per_token_cast(const void *gate_up, int64_t rows, int64_t co
 {
     return launch(true, gate_up, rows, cols, x_ld, q, q_ld, scales, s_ld, group, out_dtype, round_pow2,
                   scale_fmt, stream);
+}
+
+tk_status tk_per_token_cast_back(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void *y, int64_t y_ld,
+                                 int32_t group, int32_t out_dtype, int32_t round_pow2, void *stream)
+{
+    if (!valid_group(group) || (out_dtype != kE4M3 && out_dtype != kE2M1)) return TK_ERROR_INVALID_VALUE;
+    if (rows < 0 || cols <= 0 || cols % group != 0) return TK_ERROR_INVALID_VALUE;
+    if (x_ld < cols || y_ld < cols) return TK_ERROR_INVALID_VALUE;
+    if (cols >= (int64_t(1) << 29)) return TK_ERROR_UNSUPPORTED;
+    if (rows == 0) return TK_SUCCESS;
+    if (!x || !y) return TK_ERROR_INVALID_VALUE;
+    if (!aligned(x, 16) || (x_ld * 2) % 16 != 0 || !aligned(y, 16) || (y_ld * 2) % 16 != 0)
+        return TK_ERROR_MISALIGNED;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    tk_status st = device_info(&dev, &info);
+    if (st != TK_SUCCESS) return st;
+    static const BackTable table = make_back_table();
+    BackParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint16_t *>(y), y_ld};
+    return launch_unit_grid(reinterpret_cast<const void *>(table.fn[group_index(group)][out_dtype][round_pow2 ? 1 : 0]),
+                            rows, cols, &p, static_cast<hipStream_t>(stream));
+}
+
+tk_status tk_per_token_dequant(const void *q, int64_t rows, int64_t cols, int64_t q_ld, const void *scales,
+                               int64_t s_ld, int32_t group, int32_t in_dtype, int32_t scale_fmt, void *y,
+                               int64_t y_ld, int32_t y_dtype, void *stream)
+{
+    if (!valid_group(group) || (in_dtype != kE4M3 && in_dtype != kE2M1)) return TK_ERROR_INVALID_VALUE;
+    if ((scale_fmt != kScaleF32 && scale_fmt != kScaleUE8M0) || (y_dtype != TK_OUT_BF16 && y_dtype != TK_OUT_F32))
+        return TK_ERROR_INVALID_VALUE;
+    if (rows < 0 || cols <= 0 || cols % group != 0) return TK_ERROR_INVALID_VALUE;
+    const int64_t ngroups = cols / group;
+    if (scale_fmt == kScaleUE8M0 && ngroups % 4 != 0) return TK_ERROR_INVALID_VALUE;
+    const int64_t q_cols = (in_dtype == kE4M3) ? cols : cols / 2;
+    const int64_t s_cols = (scale_fmt == kScaleF32) ? ngroups : ngroups / 4;
+    if (q_ld < q_cols || s_ld < s_cols || y_ld < cols) return TK_ERROR_INVALID_VALUE;
+    if (cols >= (int64_t(1) << 29)) return TK_ERROR_UNSUPPORTED;
+    if (rows == 0) return TK_SUCCESS;
+    if (!q || !scales || !y) return TK_ERROR_INVALID_VALUE;
+    const int64_t qa = (in_dtype == kE4M3) ? 8 : 4;
+    const int64_t ysize = (y_dtype == TK_OUT_F32) ? 4 : 2;
+    if (!aligned(q, uintptr_t(qa)) || q_ld % qa != 0 || !aligned(scales, 4) || !aligned(y, 16) ||
+        (y_ld * ysize) % 16 != 0)
+        return TK_ERROR_MISALIGNED;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    tk_status st = device_info(&dev, &info);
+    if (st != TK_SUCCESS) return st;
+    static const DequantTable table = make_dequant_table();
+    DequantParams p{static_cast<const uint8_t *>(q), rows, cols, q_ld, scales, s_ld, y, y_ld};
+    const DequantFn fn = table.fn[group_index(group)][in_dtype][scale_fmt][y_dtype == TK_OUT_F32 ? 1 : 0];
+    return launch_unit_grid(reinterpret_cast<const void *>(fn), rows, cols, &p, static_cast<hipStream_t>(stream));
 }
 
 tk_status tk_silu32_bf16(const void *g, void *out, int64_t n, void *stream)

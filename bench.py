@@ -71,7 +71,7 @@ def summarize_pmc(workload_index, fetch_csv, write_csv):
     w = inputs.WORKLOADS[workload_index]
     fetch, write = _pmc_per_kernel(fetch_csv, "FETCH_SIZE"), _pmc_per_kernel(write_csv, "WRITE_SIZE")
     copy_k = [k for k in fetch if "copy_stream_kernel" in k]
-    cast_k = [k for k in fetch if "cast_kernel" in k]
+    cast_k = [k for k in fetch if "cast" in k and "copy_stream" not in k]
     if not copy_k or not cast_k:
         raise SystemExit("need both the cast kernel and the calibration copy in the counter runs")
     kib = float(1 << 20)
@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed steps; HBM and fabric clocks need ~15 ms of sustained load to settle")
     ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--op", choices=["cast", "dequant", "cast_back"], default="cast",
+                    help="cast (the workload's cast, fused SwiGLU for workload 3), its dequantization, "
+                         "or the fused cast-and-cast-back")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=3, help="distinct input/output sets rotated over")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -169,15 +172,39 @@ def main():
     for i in range(args.sets):
         xi = x0 if i == 0 else x0.clone()
         sets.append((xi, *tk.empty_outputs(w.rows, w.cols, w.group, w.out_dtype, w.scale_fmt, dev)))
-    fn = tk.swiglu_per_token_cast if w.swiglu else tk.per_token_cast
-    if w.swiglu:
-        tk.tk_prepare_device()
+    if args.op != "cast" and w.swiglu:
+        raise SystemExit("dequant / cast_back benchmarks take a plain cast workload (not 3)")
+    if args.op == "cast":
+        fn = tk.swiglu_per_token_cast if w.swiglu else tk.per_token_cast
+        if w.swiglu:
+            tk.tk_prepare_device()
+
+        def run(xi, qi, si, yi):
+            fn(xi, w.group, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si))
+        nbytes = w.algorithmic_bytes()
+    elif args.op == "dequant":
+        # inputs: the workload's codes and scales (made by the cast); output bf16
+        for i in range(len(sets)):
+            tk.per_token_cast(sets[i][0], w.group, w.out_dtype, w.round_pow2, w.scale_fmt,
+                              out=(sets[i][1], sets[i][2]))
+
+        def run(xi, qi, si, yi):
+            tk.per_token_dequant(qi, si, w.cols, w.group, w.out_dtype, w.scale_fmt, "bf16", out=yi)
+        nbytes = w.rows * (w.code_cols + 4 * w.scale_cols + 2 * w.cols)
+    else:
+        def run(xi, qi, si, yi):
+            tk.per_token_cast_back(xi, w.group, w.out_dtype, w.round_pow2, out=yi)
+        nbytes = w.rows * 4 * w.cols
+    if args.op != "cast":
+        sets = [(xi, qi, si, torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=dev))
+                for (xi, qi, si) in sets]
+    else:
+        sets = [(xi, qi, si, None) for (xi, qi, si) in sets]
     counter = [0]
 
     def step():
-        xi, qi, si = sets[counter[0] % len(sets)]
+        run(*sets[counter[0] % len(sets)])
         counter[0] += 1
-        fn(xi, w.group, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si))
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -199,20 +226,20 @@ def main():
     wall = time.perf_counter() - t0
     span_ms = start.elapsed_time(end)
 
-    # parity spot check of the last step's outputs against the first set's
-    # (identical inputs, so identical codes and scales)
+    # consistency check: every set holds the same inputs, so the last step's
+    # outputs equal the first set's after re-running it
     if len(sets) > 1:
         last = sets[(counter[0] - 1) % len(sets)]
-        fn(x0, w.group, w.out_dtype, w.round_pow2, w.scale_fmt, out=(sets[0][1], sets[0][2]))
+        run(*sets[0])
         torch.cuda.synchronize()
-        assert torch.equal(last[1], sets[0][1]) and torch.equal(last[2], sets[0][2])
+        outs = (1, 2) if args.op == "cast" else (3,)
+        assert all(torch.equal(last[i].view(torch.uint8), sets[0][i].view(torch.uint8)) for i in outs)
 
-    nbytes = w.algorithmic_bytes()
     ms_per_step = span_ms / args.steps
     value = nbytes * args.steps / (span_ms / 1e3) / 1e9
     avg_launch_ms = ms_per_step
     achieved = nbytes / (avg_launch_ms / 1e3) / 1e9
-    traffic = measured_traffic(w.index)
+    traffic = measured_traffic(w.index) if args.op == "cast" else None
 
     out = {
         "metric": "per-token cast GB/s (in+out bytes) and % of MI355X HBM peak; tokens/s",
@@ -230,7 +257,7 @@ def main():
         "config": {
             "workload": w.name, "rows": w.rows, "cols": w.cols, "group": w.group,
             "out_dtype": w.out_dtype, "round_pow2": w.round_pow2, "scale_fmt": w.scale_fmt,
-            "swiglu": w.swiglu, "seed": w.seed, "bytes_per_step": nbytes,
+            "swiglu": w.swiglu, "seed": w.seed, "bytes_per_step": nbytes, "op": args.op,
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.rows * args.steps / (span_ms / 1e3), 1),
@@ -253,7 +280,7 @@ def main():
         for _ in range(3):
             tk.copy_stream(src, dst)
         torch.cuda.synchronize()
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.op == "cast":
         threads = min(16, len(os.sched_getaffinity(0)))
         log(f"[bench] CPU baseline: oracle on {threads} threads")
         out["cpu_baseline"] = cpu_baseline(w, x_bits, threads)

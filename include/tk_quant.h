@@ -62,6 +62,7 @@ typedef enum tk_status {
 
 typedef enum tk_qdtype { TK_QDTYPE_E4M3 = 0, TK_QDTYPE_E2M1 = 1 } tk_qdtype;
 typedef enum tk_scale_fmt { TK_SCALE_F32 = 0, TK_SCALE_UE8M0_X4 = 1 } tk_scale_fmt;
+typedef enum tk_out_dtype { TK_OUT_BF16 = 0, TK_OUT_F32 = 1 } tk_out_dtype;
 
 /*
  * tk_per_token_cast -- cast bf16 activations to FP8 E4M3 or FP4 E2M1 codes
@@ -111,6 +112,45 @@ tk_status tk_swiglu_per_token_cast(const void *gate_up, int64_t rows, int64_t co
                                    void *q, int64_t q_ld, void *scales, int64_t s_ld,
                                    int32_t group, int32_t out_dtype, int32_t round_pow2,
                                    int32_t scale_fmt, void *stream);
+
+/*
+ * tk_per_token_dequant -- codes + scales back to activations ("Tile Kernels"
+ * (PyPI, v2.0.0), Features: casting and dequantization):
+ *     y = fl32(value(code) * s)     (value(code) exact in fp32)
+ * written as fp32 (TK_OUT_F32) or rounded to bf16, nearest with ties to even
+ * (TK_OUT_BF16).  UE8M0 bytes decode to s = 2^(byte - 127).
+ *
+ *   q        codes as tk_per_token_cast writes them, row stride q_ld bytes.
+ *   scales   fp32 [rows, cols/group] or int32 [rows, cols/group/4], row stride
+ *            s_ld elements.
+ *   group, in_dtype, scale_fmt  as for tk_per_token_cast (UE8M0 needs a
+ *            multiple of 4 groups per row).
+ *   y        bf16 or fp32 [rows, cols], row stride y_ld elements.
+ *   y_dtype  TK_OUT_BF16 or TK_OUT_F32.
+ * Alignment: q and q_ld multiples of 8 bytes (E4M3) or 4 bytes (E2M1);
+ * scales 4 bytes; y and its row stride in bytes multiples of 16.
+ * Errors as for tk_per_token_cast.
+ */
+tk_status tk_per_token_dequant(const void *q, int64_t rows, int64_t cols, int64_t q_ld,
+                               const void *scales, int64_t s_ld, int32_t group, int32_t in_dtype,
+                               int32_t scale_fmt, void *y, int64_t y_ld, int32_t y_dtype,
+                               void *stream);
+
+/*
+ * tk_per_token_cast_back -- per-token cast-and-cast-back ("TileKernels"
+ * (aiwiki.ai), Version 2.0.0): y = bf16 of the dequantized per-token cast of
+ * x, bit-identical to tk_per_token_cast followed by tk_per_token_dequant with
+ * TK_OUT_BF16, in one pass with no codes or scales written to memory.
+ *
+ *   x        bf16 [rows, cols], row stride x_ld elements.
+ *   y        bf16 [rows, cols], row stride y_ld elements (may not alias x).
+ *   group, out_dtype, round_pow2  as for tk_per_token_cast (the scale format
+ *            does not change the values).
+ * Alignment: x, y and both row strides in bytes multiples of 16.
+ */
+tk_status tk_per_token_cast_back(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
+                                 void *y, int64_t y_ld, int32_t group, int32_t out_dtype,
+                                 int32_t round_pow2, void *stream);
 
 /*
  * tk_silu32_bf16 -- diagnostic: out[i] = silu32(g[i]) for n bf16 gates, by the

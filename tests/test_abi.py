@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("tk_per_token_cast", "tk_swiglu_per_token_cast", "tk_status_string", "tk_abi_version",
-              "tk_prepare_device", "tk_silu32_bf16", "tk_copy_stream"):
+              "tk_prepare_device", "tk_silu32_bf16", "tk_copy_stream", "tk_per_token_dequant",
+              "tk_per_token_cast_back"):
         assert n in names
 
 
@@ -107,6 +108,41 @@ def test_silu_diagnostic_validation():
     assert tk.tk_silu32_bf16(0, Q, 5, 0) == INVALID
     assert tk.tk_silu32_bf16(X + 1, Q, 5, 0) == MISALIGNED
     assert tk.tk_silu32_bf16(X, Q + 2, 5, 0) == MISALIGNED
+
+
+Y = 0x40000
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(group=48), INVALID), (dict(in_dtype=2), INVALID), (dict(scale_fmt=2), INVALID),
+    (dict(y_dtype=2), INVALID), (dict(cols=200), INVALID), (dict(rows=-1), INVALID),
+    (dict(scale_fmt=1, cols=96), INVALID), (dict(q_ld=100), INVALID), (dict(s_ld=1), INVALID),
+    (dict(y_ld=100), INVALID), (dict(q=0), INVALID), (dict(y=0), INVALID), (dict(s=0), INVALID),
+    (dict(q=Q + 4), MISALIGNED), (dict(y=Y + 8), MISALIGNED), (dict(s=S + 2), MISALIGNED),
+    (dict(y_ld=260), MISALIGNED), (dict(rows=0, q=0, s=0, y=0), 0),
+])
+def test_dequant_validation(kw, want):
+    a = dict(q=Q, rows=4, cols=256, q_ld=None, s=S, s_ld=None, group=32, in_dtype=0, scale_fmt=0, y=Y,
+             y_ld=None, y_dtype=0)
+    a.update(kw)
+    q_ld = a["q_ld"] if a["q_ld"] is not None else (a["cols"] if a["in_dtype"] != 1 else a["cols"] // 2)
+    s_ld = a["s_ld"] if a["s_ld"] is not None else max(a["cols"] // 32 // (4 if a["scale_fmt"] == 1 else 1), 1)
+    y_ld = a["y_ld"] if a["y_ld"] is not None else a["cols"]
+    assert tk.tk_per_token_dequant(a["q"], a["rows"], a["cols"], q_ld, a["s"], s_ld, a["group"], a["in_dtype"],
+                                   a["scale_fmt"], a["y"], y_ld, a["y_dtype"], 0) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(group=48), INVALID), (dict(out_dtype=2), INVALID), (dict(cols=200), INVALID),
+    (dict(x_ld=100), INVALID), (dict(y_ld=100), INVALID), (dict(x=0), INVALID), (dict(y=0), INVALID),
+    (dict(x=X + 8), MISALIGNED), (dict(y=Y + 8), MISALIGNED), (dict(y_ld=260), MISALIGNED),
+    (dict(rows=0, x=0, y=0), 0),
+])
+def test_cast_back_validation(kw, want):
+    a = dict(x=X, rows=4, cols=256, x_ld=256, y=Y, y_ld=256, group=32, out_dtype=0, round_pow2=1)
+    a.update(kw)
+    assert tk.tk_per_token_cast_back(a["x"], a["rows"], a["cols"], a["x_ld"], a["y"], a["y_ld"], a["group"],
+                                     a["out_dtype"], a["round_pow2"], 0) == want
 
 
 def test_copy_stream_validation():

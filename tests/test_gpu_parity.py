@@ -285,3 +285,12 @@ def test_swiglu_dequantised_within_quantisation_bound():
     rel_l2 = np.linalg.norm(dq - h) / np.linalg.norm(h)
     log(f"[gpu] SwiGLU dequantised rel-L2 error {rel_l2:.4f}")
     assert rel_l2 < 0.05
+
+
+@pytest.mark.parametrize("group,dt,p2,sf,cols", [(16, "e4m3", False, "f32", 133120),
+                                               (16, "e2m1", True, "ue8m0", 532480)])
+def test_very_wide_rows(group, dt, p2, sf, cols):
+    """Rows whose scale row exceeds the row form's LDS budget take the
+    per-segment form; both must agree with the oracle."""
+    x = inputs.generate_small(cols, 3, cols)
+    check(x, group, dt, p2, sf, label="wide-rows")
