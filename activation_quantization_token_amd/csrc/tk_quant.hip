@@ -311,6 +311,52 @@ __device__ __forceinline__ void store_segment(const Quantized &qz, int lane, uin
     }
 }
 
+// The scale words of a whole work unit (U segments) in one store: lane j
+// fetches word j of the unit from the lane that computed it, then the first
+// U * words-per-segment lanes write them contiguously (64 words per pass).
+template <int G, int SF, int U>
+__device__ __forceinline__ void store_unit_scales(const Quantized (&qz)[U], int lane, uint32_t unit_col0,
+                                                  __amdgpu_buffer_rsrc_t srow)
+{
+    constexpr int kLanesPerGroup = G / 8;
+    constexpr int kWordsPerSeg = SF == kScaleF32 ? kSegCols / G : kSegCols / G / 4;
+    constexpr int kLanesPerWord = SF == kScaleF32 ? kLanesPerGroup : 4 * kLanesPerGroup;
+    constexpr int kUnitWords = U * kWordsPerSeg;
+    uint32_t word[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        if constexpr (SF == kScaleF32) {
+            word[k] = __float_as_uint(qz[k].s);
+        } else {
+            uint32_t b1, b2, b3;
+            if constexpr (G <= 32) {
+                b1 = dpp_mov<0x100 + kLanesPerGroup>(qz[k].e8);
+                b2 = dpp_mov<0x100 + 2 * kLanesPerGroup>(qz[k].e8);
+                b3 = dpp_mov<0x100 + 3 * kLanesPerGroup>(qz[k].e8);
+            } else {
+                b1 = shfl_u32(qz[k].e8, lane + kLanesPerGroup);
+                b2 = shfl_u32(qz[k].e8, lane + 2 * kLanesPerGroup);
+                b3 = shfl_u32(qz[k].e8, lane + 3 * kLanesPerGroup);
+            }
+            word[k] = qz[k].e8 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
+    }
+    const uint32_t first_word = SF == kScaleF32 ? unit_col0 / G : unit_col0 / (4 * G);
+#pragma unroll
+    for (int base = 0; base < kUnitWords; base += kWave) {
+        const int j = base + lane;
+        const int seg = j / kWordsPerSeg;
+        const int src = (j % kWordsPerSeg) * kLanesPerWord;
+        uint32_t v = 0;
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t t = shfl_u32(word[k], src);
+            v = (seg == k) ? t : v;
+        }
+        if (j < kUnitWords) store_scale(srow, (first_word + uint32_t(j)) * 4u, v);
+    }
+}
+
 template <int G, int QD, bool POW2, int SF>
 __device__ __forceinline__ void cast_segment(const float (&x)[8], uint32_t amax_bits, int lane, uint32_t col,
                                              __amdgpu_buffer_rsrc_t qrow, __amdgpu_buffer_rsrc_t srow)
@@ -666,6 +712,7 @@ __global__ __launch_bounds__(kWave * WPB) void swiglu_cast_kernel(CastParams p)
         }
         __amdgpu_buffer_rsrc_t qrow, srow;
         output_rows<G, QD, SF>(p, un.row, qrow, srow);
+        Quantized qz[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             float u[8], h[8];
@@ -691,8 +738,11 @@ __global__ __launch_bounds__(kWave * WPB) void swiglu_cast_kernel(CastParams p)
                     amax = max(amax, __float_as_uint(h[i]) & 0x7FFFFFFFu);
                 }
             }
-            cast_segment<G, QD, POW2, SF>(h, amax, lane, un.col0 + k * kSegCols, qrow, srow);
+            qz[k] = quantize_segment<G, QD, POW2>(h, amax);
+            if constexpr (QD == kE4M3) store8(qrow, un.col0 + k * kSegCols, qz[k].codes);
+            else store4(qrow, (un.col0 + k * kSegCols) / 2, qz[k].codes.x);
         }
+        store_unit_scales<G, SF, U>(qz, lane, un.col0 - uint32_t(lane) * 8u, srow);
     }
 }
 
@@ -780,7 +830,7 @@ using KernelFn = void (*)(CastParams);
 #define TK_CAST_WPB 2
 #endif
 #ifndef TK_SWIGLU_U
-#define TK_SWIGLU_U 1
+#define TK_SWIGLU_U 2
 #endif
 #ifndef TK_SWIGLU_WPB
 #define TK_SWIGLU_WPB 16
