@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     tk_abi_version,
     tk_copy_stream,
     tk_per_token_cast,
+    tk_per_token_cast_f32,
     tk_per_token_cast_back,
     tk_per_token_dequant,
     tk_prepare_device,

@@ -49,7 +49,7 @@ def load_library(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
                 f"{p} is not built; run `python -m activation_quantization_token_amd.build`")
         lib = ctypes.CDLL(str(p))
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
-        for name in ("tk_per_token_cast", "tk_swiglu_per_token_cast"):
+        for name in ("tk_per_token_cast", "tk_swiglu_per_token_cast", "tk_per_token_cast_f32"):
             fn = getattr(lib, name)
             fn.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, i32, i32, i32, i32, vp]
             fn.restype = ctypes.c_int
@@ -135,6 +135,14 @@ def tk_per_token_cast(x: int, rows: int, cols: int, x_ld: int, q: int, q_ld: int
                                             out_dtype, round_pow2, scale_fmt, stream)
 
 
+def tk_per_token_cast_f32(x: int, rows: int, cols: int, x_ld: int, q: int, q_ld: int, scales: int,
+                          s_ld: int, group: int, out_dtype: int, round_pow2: int, scale_fmt: int,
+                          stream: int) -> int:
+    """Raw C call (fp32 input) with integer pointers; returns the tk_status code."""
+    return load_library().tk_per_token_cast_f32(x, rows, cols, x_ld, q, q_ld, scales, s_ld, group,
+                                                out_dtype, round_pow2, scale_fmt, stream)
+
+
 def tk_swiglu_per_token_cast(gate_up: int, rows: int, cols: int, x_ld: int, q: int, q_ld: int,
                              scales: int, s_ld: int, group: int, out_dtype: int, round_pow2: int,
                              scale_fmt: int, stream: int) -> int:
@@ -144,9 +152,9 @@ def tk_swiglu_per_token_cast(gate_up: int, rows: int, cols: int, x_ld: int, q: i
                                                    stream)
 
 
-def _check_input(x: torch.Tensor, what: str):
-    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.dim() != 2:
-        raise TypeError(f"{what} must be a 2-D torch.bfloat16 tensor")
+def _check_input(x: torch.Tensor, what: str, dtype=torch.bfloat16):
+    if not isinstance(x, torch.Tensor) or x.dtype != dtype or x.dim() != 2:
+        raise TypeError(f"{what} must be a 2-D {dtype} tensor")
     if not x.is_cuda:
         raise TypeError(f"{what} must be on a GPU device")
     if x.stride(1) != 1:
@@ -188,7 +196,11 @@ def _run(fn, x, cols, group, out_dtype, round_pow2, scale_fmt, out, stream):
 
 def per_token_cast(x: torch.Tensor, group: int = 128, out_dtype: str = "e4m3",
                    round_pow2: bool = False, scale_fmt: str = "f32", out=None, stream=None):
-    """bf16 x [rows, cols] -> (codes uint8, scales float32 | int32), see include/tk_quant.h."""
+    """bf16 or fp32 x [rows, cols] -> (codes uint8, scales float32 | int32), see include/tk_quant.h."""
+    if isinstance(x, torch.Tensor) and x.dtype == torch.float32:
+        _check_input(x, "x", torch.float32)
+        return _run(tk_per_token_cast_f32, x, x.shape[1], group, out_dtype, round_pow2, scale_fmt, out,
+                    stream)
     _check_input(x, "x")
     return _run(tk_per_token_cast, x, x.shape[1], group, out_dtype, round_pow2, scale_fmt, out,
                 stream)

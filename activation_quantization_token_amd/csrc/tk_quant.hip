@@ -507,7 +507,7 @@ __global__ __launch_bounds__(kWave * WPB) void cast_kernel(CastParams p)
 // one coalesced store per 256 bytes after a barrier.  Workgroups take rows in
 // order (grid-stride), so the resident rows still form one compact window.
 // Wave w of the W in the workgroup converts runs w, w + W, ... of the row.
-template <int G, int QD, bool POW2, int SF, int U>
+template <int G, int QD, bool POW2, int SF, int U, bool IN_F32>
 __global__ __launch_bounds__(1024) void cast_rows_kernel(CastParams p)
 {
     extern __shared__ uint32_t row_scales[];     // the row's scale words
@@ -518,21 +518,37 @@ __global__ __launch_bounds__(1024) void cast_rows_kernel(CastParams p)
     const int runs = int((cols + U * kSegCols - 1) / (U * kSegCols));
     const uint32_t s_words = SF == kScaleF32 ? cols / G : cols / G / 4;
     constexpr int kLanesPerGroup = G / 8;
+    constexpr uint32_t kInBytes = IN_F32 ? 4u : 2u;
+    constexpr int kLoads = IN_F32 ? 2 : 1;       // 16-byte loads per lane per segment
     for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
-        const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + row * p.x_ld, cols * 2u);
+        const void *xrow_ptr = reinterpret_cast<const char *>(p.x) + row * p.x_ld * int64_t(kInBytes);
+        const __amdgpu_buffer_rsrc_t xrow = row_buffer(xrow_ptr, cols * kInBytes);
         __amdgpu_buffer_rsrc_t qrow, srow;
         output_rows<G, QD, SF>(p, row, qrow, srow);
         for (int run = wave; run < runs; run += nw) {
             const uint32_t col0 = uint32_t(run) * uint32_t(U * kSegCols) + uint32_t(lane) * 8u;
-            u32x4 w[U];
+            u32x4 w[U][kLoads];
 #pragma unroll
-            for (int k = 0; k < U; ++k) w[k] = load16(xrow, (col0 + k * kSegCols) * 2u);
+            for (int k = 0; k < U; ++k)
+#pragma unroll
+                for (int h = 0; h < kLoads; ++h) w[k][h] = load16(xrow, (col0 + k * kSegCols) * kInBytes + 16u * h);
 #pragma unroll
             for (int k = 0; k < U; ++k) {
                 const uint32_t col = col0 + k * kSegCols;
                 float x[8];
-                widen8(w[k], x);
-                const Quantized qz = quantize_segment<G, QD, POW2>(x, amax_bits_bf16x8(w[k]));
+                uint32_t amax;
+                if constexpr (IN_F32) {
+                    amax = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        x[i] = __uint_as_float(w[k][i / 4][i % 4]);
+                        amax = max(amax, w[k][i / 4][i % 4] & 0x7FFFFFFFu);
+                    }
+                } else {
+                    widen8(w[k][0], x);
+                    amax = amax_bits_bf16x8(w[k][0]);
+                }
+                const Quantized qz = quantize_segment<G, QD, POW2>(x, amax);
                 if constexpr (QD == kE4M3) store8(qrow, col, qz.codes);
                 else store4(qrow, col / 2, qz.codes.x);
                 if constexpr (SF == kScaleF32) {
@@ -854,21 +870,22 @@ struct RowTable {
     CastFn fn[4][2][3];
 };
 
-template <int G, int QD>
+template <bool IN_F32, int G, int QD>
 void fill_rows(CastFn (&t)[3])
 {
-    t[0] = cast_rows_kernel<G, QD, false, kScaleF32, kCastU>;
-    t[1] = cast_rows_kernel<G, QD, true, kScaleF32, kCastU>;
-    t[2] = cast_rows_kernel<G, QD, true, kScaleUE8M0, kCastU>;
+    t[0] = cast_rows_kernel<G, QD, false, kScaleF32, kCastU, IN_F32>;
+    t[1] = cast_rows_kernel<G, QD, true, kScaleF32, kCastU, IN_F32>;
+    t[2] = cast_rows_kernel<G, QD, true, kScaleUE8M0, kCastU, IN_F32>;
 }
 
+template <bool IN_F32>
 RowTable make_row_table()
 {
     RowTable t;
-    fill_rows<16, kE4M3>(t.fn[0][0]);  fill_rows<16, kE2M1>(t.fn[0][1]);
-    fill_rows<32, kE4M3>(t.fn[1][0]);  fill_rows<32, kE2M1>(t.fn[1][1]);
-    fill_rows<64, kE4M3>(t.fn[2][0]);  fill_rows<64, kE2M1>(t.fn[2][1]);
-    fill_rows<128, kE4M3>(t.fn[3][0]); fill_rows<128, kE2M1>(t.fn[3][1]);
+    fill_rows<IN_F32, 16, kE4M3>(t.fn[0][0]);  fill_rows<IN_F32, 16, kE2M1>(t.fn[0][1]);
+    fill_rows<IN_F32, 32, kE4M3>(t.fn[1][0]);  fill_rows<IN_F32, 32, kE2M1>(t.fn[1][1]);
+    fill_rows<IN_F32, 64, kE4M3>(t.fn[2][0]);  fill_rows<IN_F32, 64, kE2M1>(t.fn[2][1]);
+    fill_rows<IN_F32, 128, kE4M3>(t.fn[3][0]); fill_rows<IN_F32, 128, kE2M1>(t.fn[3][1]);
     return t;
 }
 
@@ -932,7 +949,7 @@ tk_status launch(bool swiglu, const void *x, int64_t rows, int64_t cols, int64_t
     const int variant = !round_pow2 ? 0 : (scale_fmt == kScaleF32 ? 1 : 2);
     const int64_t s_words = scale_fmt == kScaleF32 ? cols / group : cols / group / 4;
     if (!swiglu && kCastRows && s_words * 4 <= kRowScaleLdsBytes) {
-        static const RowTable row_table = make_row_table();
+        static const RowTable row_table = make_row_table<false>();
         const int64_t runs = (cols + kCastU * kSegCols - 1) / (kCastU * kSegCols);
         const int waves = int(runs < kRowMaxWaves ? runs : kRowMaxWaves);
         int64_t blocks = rows < int64_t(0x7FFFFFFF) ? rows : int64_t(0x7FFFFFFF);
@@ -1042,6 +1059,42 @@ tk_status tk_swiglu_per_token_cast(const void *gate_up, int64_t rows, int64_t co
 {
     return launch(true, gate_up, rows, cols, x_ld, q, q_ld, scales, s_ld, group, out_dtype, round_pow2,
                   scale_fmt, stream);
+}
+
+tk_status tk_per_token_cast_f32(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void *q,
+                                int64_t q_ld, void *scales, int64_t s_ld, int32_t group, int32_t out_dtype,
+                                int32_t round_pow2, int32_t scale_fmt, void *stream)
+{
+    // The bf16 checks apply to everything but the input's element size.
+    tk_status st = validate(x, rows, cols, x_ld, q, q_ld, scales, s_ld, group, out_dtype, round_pow2,
+                            scale_fmt, false);
+    if (st == TK_ERROR_MISALIGNED && aligned(x, 16) && (x_ld * 4) % 16 == 0) {
+        // recheck the outputs' alignment alone
+        const int64_t qa = (out_dtype == kE4M3) ? 8 : 4;
+        st = (!aligned(q, uintptr_t(qa)) || q_ld % qa != 0 || !aligned(scales, 4)) ? TK_ERROR_MISALIGNED
+                                                                                   : TK_SUCCESS;
+    }
+    if (st != TK_SUCCESS || rows == 0) return st;
+    if (!aligned(x, 16) || (x_ld * 4) % 16 != 0) return TK_ERROR_MISALIGNED;
+    const int64_t s_words = scale_fmt == kScaleF32 ? cols / group : cols / group / 4;
+    if (s_words * 4 > kRowScaleLdsBytes) return TK_ERROR_UNSUPPORTED;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    st = device_info(&dev, &info);
+    if (st != TK_SUCCESS) return st;
+    static const RowTable table = make_row_table<true>();
+    const int variant = !round_pow2 ? 0 : (scale_fmt == kScaleF32 ? 1 : 2);
+    const int64_t runs = (cols + kCastU * kSegCols - 1) / (kCastU * kSegCols);
+    const int waves = int(runs < kRowMaxWaves ? runs : kRowMaxWaves);
+    const int64_t blocks = rows < int64_t(0x7FFFFFFF) ? rows : int64_t(0x7FFFFFFF);
+    CastParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld, scales,
+                 s_ld};
+    void *args[] = {&p};
+    const CastFn fn = table.fn[group_index(group)][out_dtype][variant];
+    if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * waves), args,
+                        size_t(s_words * 4), static_cast<hipStream_t>(stream)) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    return TK_SUCCESS;
 }
 
 tk_status tk_per_token_cast_back(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void *y, int64_t y_ld,

@@ -163,3 +163,17 @@ def generate_small(seed: int, rows: int, cols: int, kind: str = "normal") -> np.
     if rows > 2:
         x[rows // 2, :] = 0.0
     return f64_to_bf16_bits(x)
+
+
+def generate_small_f32(seed: int, rows: int, cols: int) -> np.ndarray:
+    """Small seeded fp32 matrices (full 24-bit mantissas): per-row log-uniform
+    factors 10^U(-4, 3), 1 % outliers x 64, a zero row when rows > 2."""
+    rng = np.random.Generator(np.random.PCG64(20_000 + seed))
+    x = rng.standard_normal((rows, cols)) * (10.0 ** rng.uniform(-4.0, 3.0, size=rows))[:, None]
+    k = int(round(0.01 * rows * cols))
+    if k:
+        idx = rng.choice(rows * cols, k, replace=False)
+        x.reshape(-1)[idx] *= 64.0
+    if rows > 2:
+        x[rows // 2, :] = 0.0
+    return x.astype(np.float32)

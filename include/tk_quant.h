@@ -114,6 +114,19 @@ tk_status tk_swiglu_per_token_cast(const void *gate_up, int64_t rows, int64_t co
                                    int32_t scale_fmt, void *stream);
 
 /*
+ * tk_per_token_cast_f32 -- the per-token cast of fp32 activations ("TileKernels"
+ * (aiwiki.ai), Quantization: casts between BF16 or FP32 activations and
+ * low-precision formats).  Identical to tk_per_token_cast except that x is
+ * fp32 [rows, cols] with row stride x_ld elements (x and 4*x_ld multiples of
+ * 16 bytes) and is used as it is (no widening).  Rows whose scale row exceeds
+ * 32 KiB (more than 8192 scale words) return TK_ERROR_UNSUPPORTED.
+ */
+tk_status tk_per_token_cast_f32(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
+                                void *q, int64_t q_ld, void *scales, int64_t s_ld,
+                                int32_t group, int32_t out_dtype, int32_t round_pow2,
+                                int32_t scale_fmt, void *stream);
+
+/*
  * tk_per_token_dequant -- codes + scales back to activations ("Tile Kernels"
  * (PyPI, v2.0.0), Features: casting and dequantization):
  *     y = fl32(value(code) * s)     (value(code) exact in fp32)

@@ -55,7 +55,7 @@ def build() -> pathlib.Path:
 def _open(path) -> ctypes.CDLL:
     lib = ctypes.CDLL(str(path))
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
-    for name in ("oracle_per_token_cast", "oracle_swiglu_per_token_cast"):
+    for name in ("oracle_per_token_cast", "oracle_swiglu_per_token_cast", "oracle_per_token_cast_f32"):
         fn = getattr(lib, name)
         fn.argtypes = [p, i64, i64, i64, p, i64, p, i64, i32, i32, i32, i32, p]
         fn.restype = ctypes.c_int
@@ -144,6 +144,22 @@ def per_token_cast(x: np.ndarray, group: int = 128, out_dtype: str = "e4m3",
     work = np.empty(cols, dtype=np.float32)
     rc = _lib().oracle_per_token_cast(
         _ptr(x), rows, cols, x.strides[0] // 2, _ptr(q), q.shape[1], _ptr(s), s.shape[1],
+        group, _QDTYPES[out_dtype], int(bool(round_pow2)), _SCALE_FMTS[scale_fmt], _ptr(work))
+    if rc != 0:
+        raise ValueError("oracle rejected the cast arguments")
+    return q, s
+
+
+def per_token_cast_f32(x: np.ndarray, group: int = 128, out_dtype: str = "e4m3",
+                       round_pow2: bool = False, scale_fmt: str = "f32"):
+    """Oracle cast of fp32 activations x [rows, cols] -> (codes, scales)."""
+    if x.dtype != np.float32 or x.ndim != 2 or x.strides[1] != 4:
+        raise TypeError("x must be a 2-D float32 array with contiguous rows")
+    rows, cols = x.shape
+    q, s = _outputs(rows, cols, group, out_dtype, scale_fmt)
+    work = np.empty(cols, dtype=np.float32)
+    rc = _lib().oracle_per_token_cast_f32(
+        _ptr(x), rows, cols, x.strides[0] // 4, _ptr(q), q.shape[1], _ptr(s), s.shape[1],
         group, _QDTYPES[out_dtype], int(bool(round_pow2)), _SCALE_FMTS[scale_fmt], _ptr(work))
     if rc != 0:
         raise ValueError("oracle rejected the cast arguments")

@@ -234,6 +234,24 @@ int oracle_per_token_cast(const uint16_t *x, int64_t rows, int64_t cols, int64_t
     return 0;
 }
 
+/* The same cast of fp32 activations ("TileKernels" (aiwiki.ai),
+ * Quantization: casts of BF16 or FP32 activations): x fp32 [rows, cols], row
+ * stride x_ld elements; step 1 uses the values as they are. */
+int oracle_per_token_cast_f32(const float *x, int64_t rows, int64_t cols, int64_t x_ld,
+                              uint8_t *q, int64_t q_ld, void *scales, int64_t s_ld,
+                              int32_t group, int32_t qdtype, int32_t round_pow2, int32_t scale_fmt,
+                              float *work /* cols floats */)
+{
+    if (!valid_common(rows, cols, group, qdtype, round_pow2, scale_fmt)) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) work[c] = x[r * x_ld + c];
+        void *srow = (scale_fmt == ORACLE_SCALE_F32) ? (void *)((float *)scales + r * s_ld)
+                                                     : (void *)((uint32_t *)scales + r * s_ld);
+        cast_row(work, cols, q + r * q_ld, srow, group, qdtype, round_pow2, scale_fmt);
+    }
+    return 0;
+}
+
 /* gate_up: bf16 bits [rows, 2*cols]; gate = columns [0, cols), up =
  * columns [cols, 2*cols).  Outputs as in oracle_per_token_cast with cols. */
 int oracle_swiglu_per_token_cast(const uint16_t *gate_up, int64_t rows, int64_t cols, int64_t x_ld,

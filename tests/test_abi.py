@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("tk_per_token_cast", "tk_swiglu_per_token_cast", "tk_status_string", "tk_abi_version",
               "tk_prepare_device", "tk_silu32_bf16", "tk_copy_stream", "tk_per_token_dequant",
-              "tk_per_token_cast_back"):
+              "tk_per_token_cast_back", "tk_per_token_cast_f32"):
         assert n in names
 
 
@@ -143,6 +143,20 @@ def test_cast_back_validation(kw, want):
     a.update(kw)
     assert tk.tk_per_token_cast_back(a["x"], a["rows"], a["cols"], a["x_ld"], a["y"], a["y_ld"], a["group"],
                                      a["out_dtype"], a["round_pow2"], 0) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(group=48), INVALID), (dict(cols=200), INVALID), (dict(x_ld=100), INVALID), (dict(x=0), INVALID),
+    (dict(scale_fmt=1, round_pow2=0), INVALID), (dict(x=X + 8), MISALIGNED), (dict(x_ld=258), MISALIGNED),
+    (dict(q=Q + 4), MISALIGNED), (dict(rows=0, x=0, q=0, s=0), 0),
+    (dict(group=16, cols=16 * 8200, x_ld=16 * 8200, q_ld=16 * 8200, s_ld=8200), UNSUPPORTED),
+])
+def test_cast_f32_validation(kw, want):
+    a = dict(x=X, rows=4, cols=256, x_ld=256, q=Q, q_ld=256, s=S, s_ld=8, group=32, out_dtype=0, round_pow2=1,
+             scale_fmt=0)
+    a.update(kw)
+    assert tk.tk_per_token_cast_f32(a["x"], a["rows"], a["cols"], a["x_ld"], a["q"], a["q_ld"], a["s"], a["s_ld"],
+                                    a["group"], a["out_dtype"], a["round_pow2"], a["scale_fmt"], 0) == want
 
 
 def test_copy_stream_validation():

@@ -294,3 +294,25 @@ def test_very_wide_rows(group, dt, p2, sf, cols):
     per-segment form; both must agree with the oracle."""
     x = inputs.generate_small(cols, 3, cols)
     check(x, group, dt, p2, sf, label="wide-rows")
+
+
+@pytest.mark.parametrize("group,dt,p2,sf", [(g, dt, p2, sf) for g in (16, 32, 64, 128) for dt in ("e4m3", "e2m1")
+                                          for p2, sf in VARIANTS])
+@pytest.mark.parametrize("rows,extra", [(3, None), (129, 512)])
+def test_fp32_input_cast(group, dt, p2, sf, rows, extra):
+    cols = 7168 if extra is None else extra + 4 * group
+    x = inputs.generate_small_f32(rows + group, rows, cols)
+    log(f"[gpu] fp32-input cast rows={rows} cols={cols} G={group} {dt} pow2={p2} {sf}")
+    ld = cols + 4 * (1 + rows % 3)
+    buf = torch.full((rows, ld), float("nan"), dtype=torch.float32, device="cuda")
+    buf[:, :cols] = torch.from_numpy(x).cuda()
+    q = Guarded(rows, cols if dt == "e4m3" else cols // 2, torch.uint8, 24)
+    s = Guarded(rows, cols // group if sf == "f32" else cols // group // 4,
+                torch.float32 if sf == "f32" else torch.int32, 3)
+    tk.per_token_cast(buf[:, :cols], group, dt, p2, sf, out=(q.view, s.view))
+    torch.cuda.synchronize()
+    wq, ws = oracle.per_token_cast_f32(x, group, dt, p2, sf)
+    assert q.canaries_intact() and s.canaries_intact()
+    got_q, got_s = q.view.cpu().numpy(), s.view.cpu().numpy()
+    assert np.array_equal(got_q, wq), first_mismatch(got_q, wq)
+    assert np.array_equal(got_s.view(np.uint32), ws.view(np.uint32))

@@ -88,3 +88,20 @@ def test_cast_back_error_bound(w):
     bound = sc * step / 2 * (1 + 1e-5) + np.abs(yv) * 2.0**-8 + 1e-38
     assert np.all(np.abs(yv - xv) <= bound)
     assert np.array_equal(np.signbit(yv) | (yv == 0), np.signbit(xv) | (yv == 0))
+
+
+@pytest.mark.parametrize("group,dt,p2,sf", [(g, dt, p2, sf) for g in (16, 32, 64, 128) for dt in ("e4m3", "e2m1")
+                                          for p2, sf in ((False, "f32"), (True, "f32"), (True, "ue8m0"))])
+def test_fp32_input_cast_vs_library_composition(group, dt, p2, sf):
+    x = inputs.generate_small_f32(group, 7, 8 * group)
+    got = oracle.per_token_cast_f32(x, group, dt, p2, sf)
+    want = libref.cast_values(x, group, dt, p2, sf)
+    assert np.array_equal(got[0], want[0])
+    assert np.array_equal(got[1].view(np.uint32), want[1].view(np.uint32))
+
+
+def test_fp32_input_of_bf16_values_equals_bf16_cast():
+    x = inputs.generate_small(5, 9, 1024)
+    a = oracle.per_token_cast(x, 32, "e2m1", True, "ue8m0")
+    b = oracle.per_token_cast_f32(libref.widen(x), 32, "e2m1", True, "ue8m0")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
