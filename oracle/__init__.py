@@ -71,6 +71,8 @@ def _open(path) -> ctypes.CDLL:
     lib.oracle_per_token_dequant.restype = ctypes.c_int
     lib.oracle_per_token_cast_back.argtypes = [p, i64, i64, i64, p, i64, i32, i32, i32, p, p, p]
     lib.oracle_per_token_cast_back.restype = ctypes.c_int
+    lib.oracle_per_block_cast.argtypes = [p, i64, i64, i64, p, i64, p, i64, i64, i64, i32, i32, i32]
+    lib.oracle_per_block_cast.restype = ctypes.c_int
     lib.oracle_code_value_n.argtypes = [p, p, i64, i32]
     lib.oracle_code_value_n.restype = None
     lib.oracle_f32_to_bf16_n.argtypes = [p, p, i64]
@@ -277,3 +279,32 @@ def f32_to_bf16(v) -> np.ndarray:
     out = np.empty(v.shape, dtype=np.uint16)
     _lib().oracle_f32_to_bf16_n(_ptr(v), _ptr(out), v.size)
     return out
+
+
+def per_block_cast(x: np.ndarray, block_rows: int = 128, block_cols: int = 128, out_dtype: str = "e4m3",
+                   round_pow2: bool = False, scale_fmt: str = "f32"):
+    """Oracle per-block cast of bf16 bits x [rows, cols] -> (codes, scales);
+    scales [ceil(rows/block_rows), cols/block_cols] fp32 or [.., cols/block_cols/4] int32."""
+    _check_2d(x)
+    rows, cols = x.shape
+    if block_rows <= 0 or block_cols <= 0:
+        raise ValueError("block sizes must be positive")
+    qcols = cols if out_dtype == "e4m3" else cols // 2
+    q = np.zeros((rows, qcols), dtype=np.uint8)
+    nbr, nbc = -(-rows // block_rows), cols // block_cols
+    s = np.zeros((nbr, nbc), np.float32) if scale_fmt == "f32" else np.zeros((nbr, max(nbc // 4, 1)), np.int32)
+    rc = _lib().oracle_per_block_cast(_ptr(x), rows, cols, x.strides[0] // 2, _ptr(q), qcols, _ptr(s),
+                                      s.shape[1], block_rows, block_cols, _QDTYPES[out_dtype],
+                                      int(bool(round_pow2)), _SCALE_FMTS[scale_fmt])
+    if rc != 0:
+        raise ValueError("oracle rejected the per-block cast arguments")
+    return q, s
+
+
+def per_channel_cast(x: np.ndarray, out_dtype: str = "e4m3", round_pow2: bool = False,
+                     scale_fmt: str = "f32"):
+    """Oracle per-channel cast: one scale per column over all rows -> (codes,
+    scales [cols] fp32 or [cols/4] int32)."""
+    rows = x.shape[0]
+    q, s = per_block_cast(x, max(rows, 1), 1, out_dtype, round_pow2, scale_fmt)
+    return q, s.reshape(-1)

@@ -275,6 +275,64 @@ int oracle_swiglu_per_token_cast(const uint16_t *gate_up, int64_t rows, int64_t 
     return 0;
 }
 
+/* ---- per-block and per-channel casts ---------------------------------- */
+
+/* "Tile Kernels" (PyPI, v2.0.0), Features: per-block and per-channel FP8/FP4
+ * casting.  The same steps 1-6 with the amax taken over a block of
+ * block_rows x block_cols elements: rows [bi*Br, min(rows, (bi+1)*Br)) and
+ * columns [bj*Bc, (bj+1)*Bc).  The last block row may be partial; cols must be
+ * a multiple of Bc.  scales: fp32 [ceil(rows/Br), cols/Bc], or UE8M0 bytes of
+ * 4 consecutive column blocks per little-endian int32 [ceil(rows/Br),
+ * cols/Bc/4]; row stride s_ld elements.  Per-channel = Br = rows, Bc = 1.
+ * x: bf16 bits; q as for the per-token cast. */
+int oracle_per_block_cast(const uint16_t *x, int64_t rows, int64_t cols, int64_t x_ld,
+                          uint8_t *q, int64_t q_ld, void *scales, int64_t s_ld,
+                          int64_t block_rows, int64_t block_cols, int32_t qdtype,
+                          int32_t round_pow2, int32_t scale_fmt)
+{
+    if (rows < 0 || cols <= 0 || block_rows <= 0 || block_cols <= 0 || cols % block_cols != 0) return -1;
+    if (qdtype != ORACLE_E4M3 && qdtype != ORACLE_E2M1) return -1;
+    if (qdtype == ORACLE_E2M1 && cols % 2 != 0) return -1;
+    int64_t nbc = cols / block_cols;
+    if (scale_fmt == ORACLE_SCALE_UE8M0_X4 && (!round_pow2 || nbc % 4 != 0)) return -1;
+    if (scale_fmt != ORACLE_SCALE_F32 && scale_fmt != ORACLE_SCALE_UE8M0_X4) return -1;
+    int64_t nbr = (rows + block_rows - 1) / block_rows;
+    for (int64_t r = 0; r < rows; ++r)
+        if (qdtype == ORACLE_E2M1) memset(q + r * q_ld, 0, (size_t)(cols / 2));
+    for (int64_t bi = 0; bi < nbr; ++bi) {
+        int64_t r0 = bi * block_rows, r1 = r0 + block_rows < rows ? r0 + block_rows : rows;
+        if (scale_fmt == ORACLE_SCALE_UE8M0_X4) memset((uint32_t *)scales + bi * s_ld, 0, (size_t)(nbc / 4) * 4);
+        for (int64_t bj = 0; bj < nbc; ++bj) {
+            int64_t c0 = bj * block_cols;
+            float amax = 0.0f;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c0 + block_cols; ++c) {
+                    float a = fabsf(bf16_to_f32(x[r * x_ld + c]));
+                    if (a > amax) amax = a;
+                }
+            uint8_t e8 = 0;
+            float s = oracle_group_scale(amax, qdtype, round_pow2, &e8);
+            if (scale_fmt == ORACLE_SCALE_F32) {
+                ((float *)scales)[bi * s_ld + bj] = s;
+            } else {
+                uint32_t *dw = (uint32_t *)scales + bi * s_ld + bj / 4;
+                *dw |= (uint32_t)e8 << (8 * (bj % 4));
+            }
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c0 + block_cols; ++c) {
+                    float v = bf16_to_f32(x[r * x_ld + c]) / s;
+                    if (qdtype == ORACLE_E4M3) {
+                        q[r * q_ld + c] = oracle_encode_e4m3(v);
+                    } else {
+                        uint8_t nib = oracle_encode_e2m1(v);
+                        q[r * q_ld + c / 2] |= (uint8_t)((c % 2 == 0) ? nib : (nib << 4));
+                    }
+                }
+        }
+    }
+    return 0;
+}
+
 /* ---- dequantization and cast-back ------------------------------------ */
 
 /* fp32 -> bf16 bit pattern, round to nearest, ties to even (finite inputs

@@ -168,3 +168,33 @@ def per_token_dequant(q, scales, cols, group, in_dtype, scale_fmt, out="bf16"):
 def per_token_cast_back(x_bits, group, out_dtype, round_pow2):
     q, s = per_token_cast(x_bits, group, out_dtype, round_pow2, "f32")
     return per_token_dequant(q, s, x_bits.shape[1], group, out_dtype, "f32", "bf16")
+
+
+def block_cast_values(x: np.ndarray, block_rows: int, block_cols: int, out_dtype: str, round_pow2: bool,
+                      scale_fmt: str):
+    """Cast fp32 values x [rows, cols] with one scale per block of block_rows x
+    block_cols elements (last block row partial) -> (codes, scales)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    nbr, nbc = -(-rows // block_rows), cols // block_cols
+    amax = np.zeros((nbr, nbc), np.float32)
+    for bi in range(nbr):
+        sl = np.abs(x[bi * block_rows:(bi + 1) * block_rows]).reshape(-1, nbc, block_cols)
+        amax[bi] = sl.max(axis=(0, 2))
+    s = (np.maximum(amax, FLOOR) / D_OF[out_dtype]).astype(np.float32)
+    if round_pow2:
+        s = pow2_ceil(s)
+    s_full = np.repeat(np.repeat(s, block_rows, axis=0)[:rows], block_cols, axis=1)
+    v = (x / s_full).astype(np.float32)
+    if out_dtype == "e4m3":
+        q = e4m3_codes(v)
+    else:
+        n = e2m1_codes(v)
+        q = (n[:, 0::2] | (n[:, 1::2] << 4)).astype(np.uint8)
+    if scale_fmt == "f32":
+        return q, s
+    return q, np.ascontiguousarray(ue8m0_bytes(s)).view(np.int32).reshape(nbr, nbc // 4)
+
+
+def per_block_cast(x_bits, block_rows=128, block_cols=128, out_dtype="e4m3", round_pow2=False, scale_fmt="f32"):
+    return block_cast_values(widen(x_bits), block_rows, block_cols, out_dtype, round_pow2, scale_fmt)

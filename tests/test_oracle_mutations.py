@@ -13,6 +13,7 @@ import pathlib
 import pytest
 
 import oracle
+import test_oracle_block_pins as bpins
 import test_oracle_dequant_pins as dpins
 import test_oracle_pins as pins
 
@@ -48,6 +49,14 @@ MUTATIONS = [
     ("dequant UE8M0 exponent off by one", "s = f32_from_bits(e << 23);", "s = f32_from_bits((e + 1) << 23);", None),
     ("dequant nibbles swapped", "code = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);",
      "code = (c % 2 == 1) ? (byte & 0xF) : (byte >> 4);", None),
+    ("block amax over its first row only",
+     "for (int64_t r = r0; r < r1; ++r)\n                for (int64_t c = c0; c < c0 + block_cols; ++c) {\n                    float a",
+     "for (int64_t r = r0; r < r0 + 1; ++r)\n                for (int64_t c = c0; c < c0 + block_cols; ++c) {\n                    float a", None),
+    ("block rows rounded down", "int64_t nbr = (rows + block_rows - 1) / block_rows;",
+     "int64_t nbr = rows / block_rows;", None),
+    ("block UE8M0 big-endian", "<< (8 * (bj % 4))", "<< (8 * (3 - bj % 4))", None),
+    ("block amax over one column", "for (int64_t c = c0; c < c0 + block_cols; ++c) {\n                    float a",
+     "for (int64_t c = c0; c < c0 + 1; ++c) {\n                    float a", None),
     ("decode drops the sign", "return (float)((code & 0x80) ? -m : m);", "return (float)m;", None),
 ]
 
@@ -62,6 +71,8 @@ def _checks():
             lambda: dpins.test_dequant_vs_library_composition(32, "e2m1", "ue8m0", True, "bf16"),
             lambda: dpins.test_dequant_vs_library_composition(128, "e4m3", "f32", False, "f32"),
             lambda: dpins.test_cast_back_vs_library_composition(64, "e4m3", True),
+            lambda: bpins.test_per_block_vs_library_composition("e4m3", True, "ue8m0", 32, 32, 37),
+            lambda: bpins.test_per_block_vs_library_composition("e2m1", False, "f32", 16, 64, 37),
             lambda: pins.test_whole_tensor_vs_library_composition(32, "e2m1", True, "ue8m0", 3, 4),
             lambda: pins.test_whole_tensor_division_hard_cases("e4m3"),
             pins.test_e4m3_exhaustive_bf16_times_pow2_vs_torch,
