@@ -13,6 +13,8 @@ from .binding import (  # noqa: F401
     copy_stream,
     empty_outputs,
     load_library,
+    per_block_cast,
+    per_channel_cast,
     per_token_cast,
     per_token_cast_back,
     per_token_dequant,
@@ -20,6 +22,9 @@ from .binding import (  # noqa: F401
     swiglu_per_token_cast,
     tk_abi_version,
     tk_copy_stream,
+    tk_per_block_cast,
+    tk_per_channel_cast,
+    tk_per_channel_workspace_bytes,
     tk_per_token_cast,
     tk_per_token_cast_f32,
     tk_per_token_cast_back,

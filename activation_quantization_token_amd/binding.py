@@ -57,6 +57,12 @@ def load_library(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
         lib.tk_per_token_dequant.restype = ctypes.c_int
         lib.tk_per_token_cast_back.argtypes = [vp, i64, i64, i64, vp, i64, i32, i32, i32, vp]
         lib.tk_per_token_cast_back.restype = ctypes.c_int
+        lib.tk_per_block_cast.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, i64, i64, i32, i32, i32, vp]
+        lib.tk_per_block_cast.restype = ctypes.c_int
+        lib.tk_per_channel_workspace_bytes.argtypes = [i64, i64]
+        lib.tk_per_channel_workspace_bytes.restype = i64
+        lib.tk_per_channel_cast.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, i64, i32, i32, i32, vp]
+        lib.tk_per_channel_cast.restype = ctypes.c_int
         lib.tk_silu32_bf16.argtypes = [vp, vp, i64, vp]
         lib.tk_silu32_bf16.restype = ctypes.c_int
         lib.tk_copy_stream.argtypes = [vp, vp, i64, vp]
@@ -264,3 +270,90 @@ def per_token_cast_back(x: torch.Tensor, group: int = 128, out_dtype: str = "e4m
     _check(tk_per_token_cast_back(x.data_ptr(), rows, cols, x.stride(0), y.data_ptr(), y.stride(0), group,
                                   QDTYPES[out_dtype], int(bool(round_pow2)), _stream_handle(stream, x.device)))
     return y
+
+
+def tk_per_block_cast(x: int, rows: int, cols: int, x_ld: int, q: int, q_ld: int, scales: int, s_ld: int,
+                      block_rows: int, block_cols: int, out_dtype: int, round_pow2: int, scale_fmt: int,
+                      stream: int) -> int:
+    """Raw C call with integer pointers; returns the tk_status code."""
+    return load_library().tk_per_block_cast(x, rows, cols, x_ld, q, q_ld, scales, s_ld, block_rows, block_cols,
+                                            out_dtype, round_pow2, scale_fmt, stream)
+
+
+def tk_per_channel_workspace_bytes(rows: int, cols: int) -> int:
+    return int(load_library().tk_per_channel_workspace_bytes(rows, cols))
+
+
+def tk_per_channel_cast(x: int, rows: int, cols: int, x_ld: int, q: int, q_ld: int, scales: int, workspace: int,
+                        workspace_bytes: int, out_dtype: int, round_pow2: int, scale_fmt: int, stream: int) -> int:
+    """Raw C call with integer pointers; returns the tk_status code."""
+    return load_library().tk_per_channel_cast(x, rows, cols, x_ld, q, q_ld, scales, workspace, workspace_bytes,
+                                              out_dtype, round_pow2, scale_fmt, stream)
+
+
+def _check_formats(out_dtype: str, scale_fmt: str):
+    if out_dtype not in QDTYPES or scale_fmt not in SCALE_FMTS:
+        raise ValueError("out_dtype must be 'e4m3'|'e2m1' and scale_fmt 'f32'|'ue8m0'")
+
+
+def per_block_cast(x: torch.Tensor, block_rows: int = 128, block_cols: int = 128, out_dtype: str = "e4m3",
+                   round_pow2: bool = False, scale_fmt: str = "f32", out=None, stream=None):
+    """bf16 x [rows, cols] -> (codes, scales) with one scale per block_rows x
+    block_cols block; scales [ceil(rows/block_rows), cols/block_cols] float32
+    or [.., cols/block_cols/4] int32 (UE8M0)."""
+    _check_input(x, "x")
+    _check_formats(out_dtype, scale_fmt)
+    rows, cols = x.shape
+    if block_rows <= 0 or block_cols not in GROUPS or cols % block_cols:
+        raise ValueError("block_rows must be positive and block_cols one of 16/32/64/128 dividing cols")
+    nbr, nbc = -(-rows // block_rows), cols // block_cols
+    if out is None:
+        if scale_fmt == "ue8m0" and nbc % 4:
+            raise ValueError("ue8m0 scales need a multiple of 4 column blocks")
+        q = torch.empty((rows, cols if out_dtype == "e4m3" else cols // 2), dtype=torch.uint8, device=x.device)
+        s = (torch.empty((nbr, nbc), dtype=torch.float32, device=x.device) if scale_fmt == "f32"
+             else torch.empty((nbr, nbc // 4), dtype=torch.int32, device=x.device))
+    else:
+        q, s = out
+    for t in (q, s):
+        if t.device != x.device or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("outputs must be 2-D, row-contiguous, on the input's device")
+    if q.shape[0] != rows or s.shape[0] != nbr:
+        raise ValueError("outputs have the wrong number of rows")
+    _check(tk_per_block_cast(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0), s.data_ptr(),
+                             s.stride(0), block_rows, block_cols, QDTYPES[out_dtype], int(bool(round_pow2)),
+                             SCALE_FMTS[scale_fmt], _stream_handle(stream, x.device)))
+    return q, s
+
+
+def per_channel_cast(x: torch.Tensor, out_dtype: str = "e4m3", round_pow2: bool = False, scale_fmt: str = "f32",
+                     out=None, workspace: torch.Tensor | None = None, stream=None):
+    """bf16 x [rows, cols] -> (codes, scales) with one scale per column;
+    scales [cols] float32 or [cols/4] int32 (UE8M0).  `workspace` (a GPU
+    tensor of at least tk_per_channel_workspace_bytes(rows, cols) bytes) is
+    allocated when not given."""
+    _check_input(x, "x")
+    _check_formats(out_dtype, scale_fmt)
+    rows, cols = x.shape
+    if out is None:
+        if cols % 8:
+            raise ValueError("cols must be a multiple of 8")
+        q = torch.empty((rows, cols if out_dtype == "e4m3" else cols // 2), dtype=torch.uint8, device=x.device)
+        s = (torch.empty((cols,), dtype=torch.float32, device=x.device) if scale_fmt == "f32"
+             else torch.empty((cols // 4,), dtype=torch.int32, device=x.device))
+    else:
+        q, s = out
+    if q.device != x.device or q.dim() != 2 or q.stride(1) != 1 or q.shape[0] != rows:
+        raise ValueError("codes must be 2-D, row-contiguous, on the input's device")
+    if s.device != x.device or not s.is_contiguous():
+        raise ValueError("scales must be contiguous on the input's device")
+    need = tk_per_channel_workspace_bytes(rows, cols)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    _check(tk_per_channel_cast(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0), s.data_ptr(),
+                               workspace.data_ptr(), ws_bytes, QDTYPES[out_dtype], int(bool(round_pow2)),
+                               SCALE_FMTS[scale_fmt], _stream_handle(stream, x.device)))
+    return q, s

@@ -1,0 +1,469 @@
+// tk_block.hip -- gfx950 kernels and C ABI for the per-block and per-channel
+// casts ("Tile Kernels" (PyPI, v2.0.0), Features: per-token, per-block and
+// per-channel FP8/FP4 casting).  The arithmetic is the per-token cast's
+// (include/tk_quant.h) with the |max| taken over a block of rows x channels,
+// or over a whole column.
+//
+// Per-block design.  A workgroup owns one block row (block_rows <= 128 rows)
+// times one stripe of 512 columns.  Each of its waves loads up to 8 rows of
+// the stripe (one 16-byte load, 8 bf16, per lane per row; 1 KiB contiguous
+// per wave instruction) into registers, reduces |max| over its rows and over
+// the G/8 lanes of each block column with DPP, and the waves combine their
+// maxima through a small LDS table.  The data never leaves registers, so
+// every element is read once and written once.
+//
+// Per-channel design.  The |max| of a column needs every row before any code
+// can be written, so the cast takes two passes over x:
+//   1. channel_amax_kernel: workgroups own (row chunk, 512-column stripe)
+//      tiles and write the chunk's column maxima (bf16 magnitude bits) to a
+//      caller-provided workspace [chunks, cols];
+//   2. channel_scale_kernel: the maxima of each column over the chunks ->
+//      scales (written to the output);
+//   3. channel_cast_kernel: every element against its column's scale.  Its
+//      workgroups take the row chunks in reverse order, so the rows the first
+//      pass read last, the ones most likely still in the 256 MB Infinity
+//      Cache, are read first.
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "tk_device.h"
+#include "tk_host.h"
+
+namespace {
+
+constexpr int kBlockRowsPerWave = 8;
+constexpr int kMaxBlockRows = 128;
+constexpr int kMaxBlockWaves = kMaxBlockRows / kBlockRowsPerWave;
+
+struct BlockParams {
+    const uint16_t *x;   // bf16 bits
+    int64_t rows, cols, x_ld;
+    uint8_t *q;
+    int64_t q_ld;
+    void *s;
+    int64_t s_ld;
+    int64_t block_rows;
+};
+
+template <int BC, int QD, bool POW2, int SF>
+__global__ __launch_bounds__(kWave * kMaxBlockWaves) void block_cast_kernel(BlockParams p)
+{
+    constexpr int kLanesPerBlock = BC / 8;
+    constexpr int kBlocksPerStripe = kSegCols / BC;
+    __shared__ uint32_t wave_max[kMaxBlockWaves][kBlocksPerStripe];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = int(blockDim.x) >> 6;
+    const uint32_t cols = uint32_t(p.cols);
+    const int64_t stripes = (p.cols + kSegCols - 1) / kSegCols;
+    const int64_t bi = int64_t(blockIdx.x) / stripes;
+    const uint32_t stripe = uint32_t(int64_t(blockIdx.x) - bi * stripes);
+    const int64_t r0 = bi * p.block_rows;
+    const int64_t r1 = r0 + p.block_rows < p.rows ? r0 + p.block_rows : p.rows;
+    const int64_t wr0 = r0 + int64_t(wave) * kBlockRowsPerWave;   // this wave's first row
+    const uint32_t col = stripe * uint32_t(kSegCols) + uint32_t(lane) * 8u;
+
+    u32x4 w[kBlockRowsPerWave];
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < kBlockRowsPerWave; ++k) {
+        w[k] = u32x4{0u, 0u, 0u, 0u};
+        if (wr0 + k < r1) {                      // wave-uniform
+            const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + (wr0 + k) * p.x_ld, cols * 2u);
+            w[k] = load16(xrow, col * 2u);
+            m = max(m, amax_bits_bf16x8(w[k]));
+        }
+    }
+    m = group_max<BC>(m);
+    if (nw > 1) {
+        if ((lane % kLanesPerBlock) == 0) wave_max[wave][lane / kLanesPerBlock] = m;
+        __syncthreads();
+        m = 0;
+        for (int v = 0; v < nw; ++v) m = max(m, wave_max[v][lane / kLanesPerBlock]);
+    }
+
+    const Scale<QD, POW2> sc = group_scale<QD, POW2>(m);
+#pragma unroll
+    for (int k = 0; k < kBlockRowsPerWave; ++k) {
+        if (wr0 + k < r1) {
+            float x[8], v[8];
+            widen8(w[k], x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = scaled<QD, POW2>(x[i], sc.s, sc.inv);
+            const u32x2 codes = encode8<QD>(v);
+            const uint32_t qbytes = QD == kE4M3 ? cols : cols / 2;
+            const __amdgpu_buffer_rsrc_t qrow = row_buffer(p.q + (wr0 + k) * p.q_ld, qbytes);
+            if constexpr (QD == kE4M3) store8(qrow, col, codes);
+            else store4(qrow, col / 2, codes.x);
+        }
+    }
+
+    if (wave == 0) {
+        const uint32_t nbc = cols / BC;
+        if constexpr (SF == kScaleF32) {
+            const __amdgpu_buffer_rsrc_t srow = row_buffer(static_cast<float *>(p.s) + bi * p.s_ld, nbc * 4u);
+            if ((lane % kLanesPerBlock) == 0) store_scale(srow, (col / BC) * 4u, __float_as_uint(sc.s));
+        } else {
+            const __amdgpu_buffer_rsrc_t srow = row_buffer(static_cast<uint32_t *>(p.s) + bi * p.s_ld, nbc);
+            const uint32_t word = pack_e8_word<BC>(sc.e8, lane);
+            if ((lane % (4 * kLanesPerBlock)) == 0) store_scale(srow, (col / (4 * BC)) * 4u, word);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-channel cast.
+
+#ifndef TK_CHANNEL_WPB
+#define TK_CHANNEL_WPB 8
+#endif
+#ifndef TK_CHANNEL_UNROLL
+#define TK_CHANNEL_UNROLL 4
+#endif
+constexpr int kChannelWPB = TK_CHANNEL_WPB;        // waves per workgroup
+constexpr int kChannelUnroll = TK_CHANNEL_UNROLL;  // rows in flight per wave
+constexpr int64_t kChannelMinChunkRows = 64;
+constexpr int64_t kChannelMaxChunks = 32;
+
+struct ChannelParams {
+    const uint16_t *x;
+    int64_t rows, cols, x_ld;
+    uint8_t *q;
+    int64_t q_ld;
+    void *s;
+    uint16_t *ws;          // [chunks, cols] bf16 magnitude bits
+    int64_t chunk_rows, chunks;
+};
+
+// Pass 1: the |max| of each column over one chunk of rows.
+__global__ __launch_bounds__(kWave * kChannelWPB) void channel_amax_kernel(ChannelParams p)
+{
+    __shared__ u32x4 part[kChannelWPB][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t cols = uint32_t(p.cols);
+    const int64_t stripes = (p.cols + kSegCols - 1) / kSegCols;
+    const int64_t chunk = int64_t(blockIdx.x) / stripes;
+    const uint32_t stripe = uint32_t(int64_t(blockIdx.x) - chunk * stripes);
+    const int64_t c0 = chunk * p.chunk_rows;
+    const int64_t c1 = c0 + p.chunk_rows < p.rows ? c0 + p.chunk_rows : p.rows;
+    const uint32_t col = stripe * uint32_t(kSegCols) + uint32_t(lane) * 8u;
+    // Running maxima of |x| as bf16 magnitudes, two per word (unsigned
+    // 16-bit order is numeric order for them).
+    u16x2 mx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx[j] = u16x2{0, 0};
+    const u16x2 mag{0x7FFF, 0x7FFF};
+    for (int64_t r = c0 + wave; r < c1; r += int64_t(kChannelWPB) * kChannelUnroll) {
+        u32x4 w[kChannelUnroll];
+#pragma unroll
+        for (int k = 0; k < kChannelUnroll; ++k) {
+            const int64_t row = r + int64_t(k) * kChannelWPB;
+            w[k] = u32x4{0u, 0u, 0u, 0u};
+            if (row < c1) w[k] = load16(row_buffer(p.x + row * p.x_ld, cols * 2u), col * 2u);
+        }
+#pragma unroll
+        for (int k = 0; k < kChannelUnroll; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                mx[j] = __builtin_elementwise_max(mx[j], __builtin_bit_cast(u16x2, uint32_t(w[k][j])) & mag);
+    }
+    u32x4 mine;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mine[j] = __builtin_bit_cast(uint32_t, mx[j]);
+    part[wave][lane] = mine;
+    __syncthreads();
+    if (wave == 0) {
+        u16x2 t[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[j] = mx[j];
+        for (int v = 1; v < kChannelWPB; ++v) {
+            const u32x4 o = part[v][lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t[j] = __builtin_elementwise_max(t[j], __builtin_bit_cast(u16x2, uint32_t(o[j])));
+        }
+        u32x4 out;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = __builtin_bit_cast(uint32_t, t[j]);
+        store16(row_buffer(p.ws + chunk * p.cols, cols * 2u), col * 2u, out);
+    }
+}
+
+// Pass 2: one thread per 8 columns: the maximum over the chunks -> scales.
+constexpr int kChannelScaleBlock = 256;
+
+template <int QD, bool POW2, int SF>
+__global__ __launch_bounds__(kChannelScaleBlock) void channel_scale_kernel(ChannelParams p)
+{
+    const int64_t t = int64_t(blockIdx.x) * kChannelScaleBlock + threadIdx.x;
+    const uint32_t cols = uint32_t(p.cols);
+    const uint32_t col = uint32_t(t) * 8u;
+    if (col >= cols) return;
+    u16x2 mx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx[j] = u16x2{0, 0};
+    for (int64_t c = 0; c < p.chunks; ++c) {
+        const u32x4 w = load16(row_buffer(p.ws + c * p.cols, cols * 2u), col * 2u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx[j] = __builtin_elementwise_max(mx[j], __builtin_bit_cast(u16x2, uint32_t(w[j])));
+    }
+    float s[8];
+    uint32_t e8[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t amax_bits = uint32_t(h ? mx[j].y : mx[j].x) << 16;
+            const Scale<QD, POW2> sc = group_scale<QD, POW2>(amax_bits);
+            s[2 * j + h] = sc.s;
+            e8[2 * j + h] = sc.e8;
+        }
+    }
+    if constexpr (SF == kScaleF32) {
+        const __amdgpu_buffer_rsrc_t srow = row_buffer(p.s, cols * 4u);
+        u32x4 a, b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i] = __float_as_uint(s[i]);
+            b[i] = __float_as_uint(s[4 + i]);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(a, srow, int(col * 4u), 0, TK_SCALE_STORE_POLICY);
+        __builtin_amdgcn_raw_buffer_store_b128(b, srow, int(col * 4u + 16u), 0, TK_SCALE_STORE_POLICY);
+    } else {
+        const __amdgpu_buffer_rsrc_t srow = row_buffer(p.s, cols);
+        const u32x2 v{e8[0] | (e8[1] << 8) | (e8[2] << 16) | (e8[3] << 24),
+                      e8[4] | (e8[5] << 8) | (e8[6] << 16) | (e8[7] << 24)};
+        __builtin_amdgcn_raw_buffer_store_b64(v, srow, int(col), 0, TK_SCALE_STORE_POLICY);
+    }
+}
+
+// Pass 3: codes against the column scales, row chunks in reverse order.
+template <int QD, bool POW2, int SF>
+__global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(ChannelParams p)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t cols = uint32_t(p.cols);
+    const int64_t stripes = (p.cols + kSegCols - 1) / kSegCols;
+    const int64_t chunk = p.chunks - 1 - int64_t(blockIdx.x) / stripes;
+    const uint32_t stripe = uint32_t(int64_t(blockIdx.x) % stripes);
+    const int64_t c0 = chunk * p.chunk_rows;
+    const int64_t c1 = c0 + p.chunk_rows < p.rows ? c0 + p.chunk_rows : p.rows;
+    const uint32_t col = stripe * uint32_t(kSegCols) + uint32_t(lane) * 8u;
+    // This lane's 8 column scales (and, for powers of two, their exact
+    // reciprocals), read back from the scale output.
+    float s[8], inv[8];
+    if constexpr (SF == kScaleF32) {
+        const __amdgpu_buffer_rsrc_t srow = row_buffer(p.s, cols * 4u);
+        const u32x4 a = load16(srow, col * 4u), b = load16(srow, col * 4u + 16u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[i] = __uint_as_float(a[i]);
+            s[4 + i] = __uint_as_float(b[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) inv[i] = __uint_as_float(0x7F000000u - (__float_as_uint(s[i]) & 0x7F800000u));
+    } else {
+        const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(row_buffer(p.s, cols), int(col), 0, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t E = (e[i / 4] >> (8 * (i % 4))) & 0xFFu;
+            s[i] = __uint_as_float(E << 23);
+            inv[i] = __uint_as_float((254u - E) << 23);
+        }
+    }
+    const uint32_t qbytes = QD == kE4M3 ? cols : cols / 2;
+    for (int64_t r = c0 + wave; r < c1; r += int64_t(kChannelWPB) * kChannelUnroll) {
+        u32x4 w[kChannelUnroll];
+#pragma unroll
+        for (int k = 0; k < kChannelUnroll; ++k) {
+            const int64_t row = r + int64_t(k) * kChannelWPB;
+            w[k] = u32x4{0u, 0u, 0u, 0u};
+            if (row < c1) w[k] = load16(row_buffer(p.x + row * p.x_ld, cols * 2u), col * 2u);
+        }
+#pragma unroll
+        for (int k = 0; k < kChannelUnroll; ++k) {
+            const int64_t row = r + int64_t(k) * kChannelWPB;
+            if (row < c1) {
+                float x[8], v[8];
+                widen8(w[k], x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = scaled<QD, POW2>(x[i], s[i], inv[i]);
+                const u32x2 codes = encode8<QD>(v);
+                const __amdgpu_buffer_rsrc_t qrow = row_buffer(p.q + row * p.q_ld, qbytes);
+                if constexpr (QD == kE4M3) store8(qrow, col, codes);
+                else store4(qrow, col / 2, codes.x);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+using BlockFn = void (*)(BlockParams);
+using ChannelFn = void (*)(ChannelParams);
+
+struct BlockTable {
+    BlockFn fn[4][2][3];         // [block_cols index][code format][variant]
+};
+struct ChannelTable {
+    ChannelFn scale[2][3], cast[2][3];   // [code format][variant]
+};
+
+template <int BC, int QD>
+void fill_block(BlockFn (&t)[3])
+{
+    t[0] = block_cast_kernel<BC, QD, false, kScaleF32>;
+    t[1] = block_cast_kernel<BC, QD, true, kScaleF32>;
+    t[2] = block_cast_kernel<BC, QD, true, kScaleUE8M0>;
+}
+
+BlockTable make_block_table()
+{
+    BlockTable t;
+    fill_block<16, kE4M3>(t.fn[0][0]);  fill_block<16, kE2M1>(t.fn[0][1]);
+    fill_block<32, kE4M3>(t.fn[1][0]);  fill_block<32, kE2M1>(t.fn[1][1]);
+    fill_block<64, kE4M3>(t.fn[2][0]);  fill_block<64, kE2M1>(t.fn[2][1]);
+    fill_block<128, kE4M3>(t.fn[3][0]); fill_block<128, kE2M1>(t.fn[3][1]);
+    return t;
+}
+
+template <int QD>
+void fill_channel(ChannelTable &t)
+{
+    t.scale[QD][0] = channel_scale_kernel<QD, false, kScaleF32>;
+    t.scale[QD][1] = channel_scale_kernel<QD, true, kScaleF32>;
+    t.scale[QD][2] = channel_scale_kernel<QD, true, kScaleUE8M0>;
+    t.cast[QD][0] = channel_cast_kernel<QD, false, kScaleF32>;
+    t.cast[QD][1] = channel_cast_kernel<QD, true, kScaleF32>;
+    t.cast[QD][2] = channel_cast_kernel<QD, true, kScaleUE8M0>;
+}
+
+ChannelTable make_channel_table()
+{
+    ChannelTable t;
+    fill_channel<kE4M3>(t);
+    fill_channel<kE2M1>(t);
+    return t;
+}
+
+int block_cols_index(int64_t bc) { return bc == 16 ? 0 : bc == 32 ? 1 : bc == 64 ? 2 : 3; }
+
+// Checks shared by both casts: formats, sizes, the input and code layouts.
+tk_status validate_common(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void *q, int64_t q_ld,
+                          void *scales, int32_t out_dtype, int32_t round_pow2, int32_t scale_fmt)
+{
+    if (out_dtype != kE4M3 && out_dtype != kE2M1) return TK_ERROR_INVALID_VALUE;
+    if (scale_fmt != kScaleF32 && scale_fmt != kScaleUE8M0) return TK_ERROR_INVALID_VALUE;
+    if (scale_fmt == kScaleUE8M0 && !round_pow2) return TK_ERROR_INVALID_VALUE;
+    if (rows < 0 || cols <= 0) return TK_ERROR_INVALID_VALUE;
+    const int64_t q_cols = (out_dtype == kE4M3) ? cols : cols / 2;
+    if (x_ld < cols || q_ld < q_cols) return TK_ERROR_INVALID_VALUE;
+    if (cols >= (int64_t(1) << 29)) return TK_ERROR_UNSUPPORTED;   // row byte offsets are 32-bit
+    if (rows == 0) return TK_SUCCESS;
+    if (!x || !q || !scales) return TK_ERROR_INVALID_VALUE;
+    if (!aligned(x, 16) || (x_ld * 2) % 16 != 0) return TK_ERROR_MISALIGNED;
+    const int64_t qa = (out_dtype == kE4M3) ? 8 : 4;
+    if (!aligned(q, uintptr_t(qa)) || q_ld % qa != 0) return TK_ERROR_MISALIGNED;
+    return TK_SUCCESS;
+}
+
+int64_t channel_chunk_rows(int64_t rows)
+{
+    const int64_t r = (rows + kChannelMaxChunks - 1) / kChannelMaxChunks;
+    return r > kChannelMinChunkRows ? r : kChannelMinChunkRows;
+}
+
+int64_t channel_chunks(int64_t rows)
+{
+    const int64_t cr = channel_chunk_rows(rows);
+    return (rows + cr - 1) / cr;
+}
+
+}  // namespace
+
+extern "C" {
+
+tk_status tk_per_block_cast(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void *q, int64_t q_ld,
+                            void *scales, int64_t s_ld, int64_t block_rows, int64_t block_cols, int32_t out_dtype,
+                            int32_t round_pow2, int32_t scale_fmt, void *stream)
+{
+    if (block_cols != 16 && block_cols != 32 && block_cols != 64 && block_cols != 128) return TK_ERROR_INVALID_VALUE;
+    if (block_rows <= 0) return TK_ERROR_INVALID_VALUE;
+    if (cols <= 0 || cols % block_cols != 0) return TK_ERROR_INVALID_VALUE;
+    const int64_t nbc = cols / block_cols;
+    if (scale_fmt == kScaleUE8M0 && nbc % 4 != 0) return TK_ERROR_INVALID_VALUE;
+    const int64_t s_cols = scale_fmt == kScaleUE8M0 ? nbc / 4 : nbc;
+    if (s_ld < s_cols) return TK_ERROR_INVALID_VALUE;
+    tk_status st = validate_common(x, rows, cols, x_ld, q, q_ld, scales, out_dtype, round_pow2, scale_fmt);
+    if (st != TK_SUCCESS || rows == 0) return st;
+    if (block_rows > kMaxBlockRows) return TK_ERROR_UNSUPPORTED;
+    if (!aligned(scales, 4)) return TK_ERROR_MISALIGNED;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    st = device_info(&dev, &info);
+    if (st != TK_SUCCESS) return st;
+    static const BlockTable table = make_block_table();
+    const int variant = !round_pow2 ? 0 : (scale_fmt == kScaleF32 ? 1 : 2);
+    const int64_t nbr = (rows + block_rows - 1) / block_rows;
+    const int64_t stripes = (cols + kSegCols - 1) / kSegCols;
+    const int64_t blocks = nbr * stripes;
+    if (blocks > int64_t(0x7FFFFFFF)) return TK_ERROR_UNSUPPORTED;
+    const int64_t used_rows = block_rows < rows ? block_rows : rows;
+    const int waves = int((used_rows + kBlockRowsPerWave - 1) / kBlockRowsPerWave);
+    BlockParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld, scales, s_ld,
+                  block_rows};
+    void *args[] = {&p};
+    const BlockFn fn = table.fn[block_cols_index(block_cols)][out_dtype][variant];
+    if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * waves), args, 0,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    return TK_SUCCESS;
+}
+
+int64_t tk_per_channel_workspace_bytes(int64_t rows, int64_t cols)
+{
+    if (rows <= 0 || cols <= 0) return 0;
+    return channel_chunks(rows) * cols * 2;
+}
+
+tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void *q, int64_t q_ld,
+                              void *scales, void *workspace, int64_t workspace_bytes, int32_t out_dtype,
+                              int32_t round_pow2, int32_t scale_fmt, void *stream)
+{
+    if (cols <= 0 || cols % 8 != 0) return TK_ERROR_INVALID_VALUE;
+    tk_status st = validate_common(x, rows, cols, x_ld, q, q_ld, scales, out_dtype, round_pow2, scale_fmt);
+    if (st != TK_SUCCESS || rows == 0) return st;
+    if (!workspace || workspace_bytes < tk_per_channel_workspace_bytes(rows, cols)) return TK_ERROR_INVALID_VALUE;
+    if (!aligned(scales, scale_fmt == kScaleF32 ? 16 : 8) || !aligned(workspace, 16)) return TK_ERROR_MISALIGNED;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    st = device_info(&dev, &info);
+    if (st != TK_SUCCESS) return st;
+    static const ChannelTable table = make_channel_table();
+    const int variant = !round_pow2 ? 0 : (scale_fmt == kScaleF32 ? 1 : 2);
+    const int64_t chunk_rows = channel_chunk_rows(rows), chunks = channel_chunks(rows);
+    const int64_t stripes = (cols + kSegCols - 1) / kSegCols;
+    const int64_t tiles = chunks * stripes;
+    if (tiles > int64_t(0x7FFFFFFF)) return TK_ERROR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ChannelParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld, scales,
+                    static_cast<uint16_t *>(workspace), chunk_rows, chunks};
+    void *args[] = {&p};
+    if (hipLaunchKernel(reinterpret_cast<const void *>(channel_amax_kernel), dim3(uint32_t(tiles)),
+                        dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    const int64_t scale_blocks = (cols / 8 + kChannelScaleBlock - 1) / kChannelScaleBlock;
+    if (hipLaunchKernel(reinterpret_cast<const void *>(table.scale[out_dtype][variant]), dim3(uint32_t(scale_blocks)),
+                        dim3(kChannelScaleBlock), args, 0, s) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    if (hipLaunchKernel(reinterpret_cast<const void *>(table.cast[out_dtype][variant]), dim3(uint32_t(tiles)),
+                        dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    return TK_SUCCESS;
+}
+
+}  // extern "C"

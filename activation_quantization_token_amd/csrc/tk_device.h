@@ -1,0 +1,272 @@
+// tk_device.h -- device helpers shared by the library's kernels (gfx950,
+// wave64): formats, buffer-descriptor access, cross-lane reductions, and the
+// conversion of 8 values with a known |max| to codes and a scale.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "tk_quant.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kSegCols = kWave * 8;   // columns per wave per segment
+
+constexpr int kE4M3 = TK_QDTYPE_E4M3;
+constexpr int kE2M1 = TK_QDTYPE_E2M1;
+constexpr int kScaleF32 = TK_SCALE_F32;
+constexpr int kScaleUE8M0 = TK_SCALE_UE8M0_X4;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Buffer access.  dword 3 of a gfx9-family buffer descriptor is 0x00020000
+// for raw (untyped, unswizzled) access; cache policy 2 sets the non-temporal
+// bit (nt), so streamed lines do not displace other data in L2 / the Infinity
+// Cache and a call's writes do not linger as dirty lines.
+
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), kBufferDword3);
+}
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, int(byte_off), 0, kNonTemporal);
+}
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, int(byte_off), 0, kNonTemporal);
+}
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x2 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, int(byte_off), 0, kNonTemporal);
+}
+
+// Scale rows are short (4 to 2048 bytes) and each is written in 4-to-64-byte
+// pieces by several waves; plain write-back stores let L2 merge those pieces
+// into whole lines before they go to memory.
+#ifndef TK_SCALE_STORE_POLICY
+#define TK_SCALE_STORE_POLICY 0
+#endif
+__device__ __forceinline__ void store_scale(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, int(byte_off), 0, TK_SCALE_STORE_POLICY);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers.
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v)
+{
+    // Row and bank masks full.  Lanes whose source falls outside their
+    // 16-lane row (row_shl near the row end) keep 0; no result of such a lane
+    // is used.
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over the G/8 consecutive lanes that hold one group; every lane of the
+// group receives the result.  Values are fp32 bit patterns of |x|, for which
+// unsigned order equals numeric order.
+template <int G>
+__device__ __forceinline__ uint32_t group_max(uint32_t v)
+{
+    if constexpr (G >= 16) v = max(v, dpp_mov<0xB1>(v));    // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (G >= 32) v = max(v, dpp_mov<0x4E>(v));    // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (G >= 64) v = max(v, dpp_mov<0x141>(v));   // row_half_mirror: 8-lane halves
+    if constexpr (G >= 128) v = max(v, dpp_mov<0x140>(v));  // row_mirror: 16-lane row
+    return v;
+}
+
+__device__ __forceinline__ uint32_t shfl_u32(uint32_t v, int src_lane)
+{
+    return uint32_t(__builtin_amdgcn_ds_bpermute((src_lane & 63) << 2, int(v)));
+}
+
+// ---------------------------------------------------------------------------
+// The per-segment cast: 8 fp32 values per lane (columns col .. col+7 of one
+// row) and their |max| bits -> codes in registers plus the group's scale.
+
+struct Quantized {
+    u32x2 codes;    // E4M3: 8 bytes; E2M1: 8 nibbles in codes.x
+    float s;        // the group's scale
+    uint32_t e8;    // its biased exponent byte (power-of-two scales)
+};
+
+// Scale of a group from its |max| bits: s = max(a, 1e-4f) / D, rounded up to
+// a power of two when POW2 (then e8 is its biased exponent and inv = 1/s,
+// both exact).
+template <int QD, bool POW2>
+struct Scale {
+    float s, inv;
+    uint32_t e8;
+};
+
+template <int QD, bool POW2>
+__device__ __forceinline__ Scale<QD, POW2> group_scale(uint32_t amax_bits)
+{
+    constexpr float D = (QD == kE4M3) ? 448.0f : 6.0f;
+    const float a = fmaxf(__uint_as_float(amax_bits), 1e-4f);
+    Scale<QD, POW2> r;
+    r.s = a / D;                           // IEEE fp32 division
+    r.inv = 0.0f;
+    r.e8 = 0;
+    if constexpr (POW2) {
+        // s is normal (>= 1e-4f / 448): 2^ceil(log2 s) from the exponent and
+        // mantissa fields; E lies in [105, 253], so 2^(127-E) is normal too.
+        const uint32_t b = __float_as_uint(r.s);
+        const uint32_t E = (b >> 23) + ((b & 0x7FFFFFu) != 0u);
+        r.e8 = E;
+        r.s = __uint_as_float(E << 23);
+        r.inv = __uint_as_float((254u - E) << 23);
+    }
+    return r;
+}
+
+// x / s, clamped to the format's range.  With a power-of-two scale x * 2^-e
+// is the exact quotient x / 2^e rounded once, as x / s is.
+template <int QD, bool POW2>
+__device__ __forceinline__ float scaled(float x, float s, float inv)
+{
+    constexpr float D = (QD == kE4M3) ? 448.0f : 6.0f;
+    return __builtin_amdgcn_fmed3f(POW2 ? x * inv : x / s, D, -D);
+}
+
+// 8 clamped values -> codes, nearest with ties to even, by the gfx950
+// converters: E4M3 in 8 bytes, E2M1 in 8 nibbles of the first word (value
+// 2i in the low nibble of byte i).
+template <int QD>
+__device__ __forceinline__ u32x2 encode8(const float (&v)[8])
+{
+    if constexpr (QD == kE4M3) {
+        uint32_t lo = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false));
+        lo = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], int(lo), true));
+        uint32_t hi = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false));
+        hi = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], int(hi), true));
+        return u32x2{lo, hi};
+    } else {
+        uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], 1.0f, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], 1.0f, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], 1.0f, 3);
+        return u32x2{r, 0u};
+    }
+}
+
+// 8 values whose scale group has |max| bits amax_bits (already reduced over
+// the group) -> codes and scale.
+template <int QD, bool POW2>
+__device__ __forceinline__ Quantized quantize_values(const float (&x)[8], uint32_t amax_bits)
+{
+    const Scale<QD, POW2> sc = group_scale<QD, POW2>(amax_bits);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = scaled<QD, POW2>(x[i], sc.s, sc.inv);
+    Quantized out;
+    out.s = sc.s;
+    out.e8 = sc.e8;
+    out.codes = encode8<QD>(v);
+    return out;
+}
+
+// Four consecutive groups' exponent bytes as one little-endian int32, valid
+// on the first lane of the first group (groups of G columns, G/8 lanes each).
+// For G <= 32 the four groups lie in one 16-lane DPP row and row_shl moves
+// (lane i reads lane i + N) gather them without an LDS round trip.
+template <int G>
+__device__ __forceinline__ uint32_t pack_e8_word(uint32_t e8, int lane)
+{
+    constexpr int kLanesPerGroup = G / 8;
+    uint32_t b1, b2, b3;
+    if constexpr (G <= 32) {
+        b1 = dpp_mov<0x100 + kLanesPerGroup>(e8);
+        b2 = dpp_mov<0x100 + 2 * kLanesPerGroup>(e8);
+        b3 = dpp_mov<0x100 + 3 * kLanesPerGroup>(e8);
+    } else {
+        b1 = shfl_u32(e8, lane + kLanesPerGroup);
+        b2 = shfl_u32(e8, lane + 2 * kLanesPerGroup);
+        b3 = shfl_u32(e8, lane + 3 * kLanesPerGroup);
+    }
+    return e8 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+// The same for a per-token group held by G/8 consecutive lanes: each lane
+// brings its own 8 values' |max| bits, reduced here over the group.
+template <int G, int QD, bool POW2>
+__device__ __forceinline__ Quantized quantize_segment(const float (&x)[8], uint32_t amax_bits)
+{
+    return quantize_values<QD, POW2>(x, group_max<G>(amax_bits));
+}
+
+// Code values back to fp32 (exact) with the hardware decoders, times s.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int QD>
+__device__ __forceinline__ void dequant_codes(u32x2 codes, float s, float (&y)[8])
+{
+    f32x2 d[4];
+    if constexpr (QD == kE4M3) {
+        d[0] = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes.x), false);
+        d[1] = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes.x), true);
+        d[2] = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes.y), false);
+        d[3] = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes.y), true);
+    } else {
+        d[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, 1.0f, 0);
+        d[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, 1.0f, 1);
+        d[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, 1.0f, 2);
+        d[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, 1.0f, 3);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        y[2 * k] = d[k].x * s;
+        y[2 * k + 1] = d[k].y * s;
+    }
+}
+
+// 8 fp32 -> 8 bf16 (nearest, ties to even; v_cvt_pk_bf16_f32) in 16 bytes.
+__device__ __forceinline__ u32x4 pack_bf16x8(const float (&y)[8])
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    u32x4 out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const bf16x2 p = {__bf16(y[2 * k]), __bf16(y[2 * k + 1])};
+        out[k] = __builtin_bit_cast(uint32_t, p);
+    }
+    return out;
+}
+
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, int(byte_off), 0, kNonTemporal);
+}
+
+__device__ __forceinline__ void widen8(const u32x4 &w, float (&x)[8])
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(w[k] << 16);
+        x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+}
+
+// |x| max of 8 bf16 as fp32 bits: bf16 magnitudes compare as unsigned 16-bit
+// integers, two per packed max.
+__device__ __forceinline__ uint32_t amax_bits_bf16x8(const u32x4 &w)
+{
+    const uint32_t m = 0x7FFF7FFFu;
+    const u16x2 va = __builtin_bit_cast(u16x2, uint32_t(w[0] & m)), vb = __builtin_bit_cast(u16x2, uint32_t(w[1] & m));
+    const u16x2 vc = __builtin_bit_cast(u16x2, uint32_t(w[2] & m)), vd = __builtin_bit_cast(u16x2, uint32_t(w[3] & m));
+    const u16x2 t = __builtin_elementwise_max(__builtin_elementwise_max(va, vb), __builtin_elementwise_max(vc, vd));
+    const uint32_t lo = t.x, hi = t.y;
+    return max(lo, hi) << 16;
+}
+
+}  // namespace

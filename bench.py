@@ -136,9 +136,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed steps; HBM and fabric clocks need ~15 ms of sustained load to settle")
     ap.add_argument("--workload", type=int, default=4)
-    ap.add_argument("--op", choices=["cast", "dequant", "cast_back"], default="cast",
+    ap.add_argument("--op", choices=["cast", "dequant", "cast_back", "per_block", "per_channel"], default="cast",
                     help="cast (the workload's cast, fused SwiGLU for workload 3), its dequantization, "
-                         "or the fused cast-and-cast-back")
+                         "the fused cast-and-cast-back, or the per-block / per-channel cast of the "
+                         "workload's input with its code and scale formats")
+    ap.add_argument("--block", default="128x128", help="block rows x block columns for --op per_block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=3, help="distinct input/output sets rotated over")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -191,11 +193,28 @@ def main():
         def run(xi, qi, si, yi):
             tk.per_token_dequant(qi, si, w.cols, w.group, w.out_dtype, w.scale_fmt, "bf16", out=yi)
         nbytes = w.rows * (w.code_cols + 4 * w.scale_cols + 2 * w.cols)
-    else:
+    elif args.op == "cast_back":
         def run(xi, qi, si, yi):
             tk.per_token_cast_back(xi, w.group, w.out_dtype, w.round_pow2, out=yi)
         nbytes = w.rows * 4 * w.cols
-    if args.op != "cast":
+    elif args.op == "per_block":
+        br, bc = (int(v) for v in args.block.split("x"))
+        sets = [(xi, *tk.per_block_cast(xi, br, bc, w.out_dtype, w.round_pow2, w.scale_fmt)) for (xi, _, _) in sets]
+
+        def run(xi, qi, si, yi):
+            tk.per_block_cast(xi, br, bc, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si))
+        s0 = sets[0][2]
+        nbytes = w.rows * (2 * w.cols + w.code_cols) + s0.numel() * s0.element_size()
+    else:
+        ws = torch.empty((tk.tk_per_channel_workspace_bytes(w.rows, w.cols),), dtype=torch.uint8, device=dev)
+        sets = [(xi, *tk.per_channel_cast(xi, w.out_dtype, w.round_pow2, w.scale_fmt, workspace=ws))
+                for (xi, _, _) in sets]
+
+        def run(xi, qi, si, yi):
+            tk.per_channel_cast(xi, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si), workspace=ws)
+        s0 = sets[0][2]
+        nbytes = w.rows * (2 * w.cols + w.code_cols) + s0.numel() * s0.element_size()
+    if args.op in ("dequant", "cast_back"):
         sets = [(xi, qi, si, torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=dev))
                 for (xi, qi, si) in sets]
     else:
@@ -232,7 +251,7 @@ def main():
         last = sets[(counter[0] - 1) % len(sets)]
         run(*sets[0])
         torch.cuda.synchronize()
-        outs = (1, 2) if args.op == "cast" else (3,)
+        outs = (3,) if args.op in ("dequant", "cast_back") else (1, 2)
         assert all(torch.equal(last[i].view(torch.uint8), sets[0][i].view(torch.uint8)) for i in outs)
 
     ms_per_step = span_ms / args.steps
@@ -241,8 +260,11 @@ def main():
     achieved = nbytes / (avg_launch_ms / 1e3) / 1e9
     traffic = measured_traffic(w.index) if args.op == "cast" else None
 
+    metric = "per-token cast GB/s (in+out bytes) and % of MI355X HBM peak; tokens/s"
+    if args.op != "cast":
+        metric = f"{args.op} GB/s (algorithmic in+out bytes) and % of MI355X HBM peak"
     out = {
-        "metric": "per-token cast GB/s (in+out bytes) and % of MI355X HBM peak; tokens/s",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -258,6 +280,7 @@ def main():
             "workload": w.name, "rows": w.rows, "cols": w.cols, "group": w.group,
             "out_dtype": w.out_dtype, "round_pow2": w.round_pow2, "scale_fmt": w.scale_fmt,
             "swiglu": w.swiglu, "seed": w.seed, "bytes_per_step": nbytes, "op": args.op,
+            **({"block": args.block} if args.op == "per_block" else {}),
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.rows * args.steps / (span_ms / 1e3), 1),

@@ -166,6 +166,55 @@ tk_status tk_per_token_cast_back(const void *x, int64_t rows, int64_t cols, int6
                                  int32_t round_pow2, void *stream);
 
 /*
+ * tk_per_block_cast -- the cast with one scale per block of block_rows x
+ * block_cols elements ("Tile Kernels" (PyPI, v2.0.0), Features: per-block
+ * FP8/FP4 casting).  Block (i, j) covers rows [i*block_rows,
+ * min(rows, (i+1)*block_rows)) and columns [j*block_cols, (j+1)*block_cols);
+ * a  = max(|x|) over the block, floored at 1e-4f, then s, pow2 and the codes
+ * exactly as for tk_per_token_cast.
+ *
+ *   x, rows, cols, x_ld, q, q_ld, out_dtype, round_pow2, scale_fmt
+ *            as for tk_per_token_cast (cols a multiple of block_cols; the last
+ *            block row may be partial).
+ *   scales   float [ceil(rows/block_rows), cols/block_cols] or int32
+ *            [ceil(rows/block_rows), cols/block_cols/4] (UE8M0, four blocks of
+ *            one block row per int32, block 4k+b in byte b); row stride s_ld
+ *            elements.
+ *   block_rows  1 .. 128 (larger: TK_ERROR_UNSUPPORTED).
+ *   block_cols  16, 32, 64 or 128.
+ * Alignment and errors as for tk_per_token_cast.
+ */
+tk_status tk_per_block_cast(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
+                            void *q, int64_t q_ld, void *scales, int64_t s_ld,
+                            int64_t block_rows, int64_t block_cols, int32_t out_dtype,
+                            int32_t round_pow2, int32_t scale_fmt, void *stream);
+
+/*
+ * tk_per_channel_cast -- the cast with one scale per column (channel), the
+ * |max| taken over all rows ("Tile Kernels" (PyPI, v2.0.0), Features:
+ * per-channel FP8/FP4 casting); otherwise exactly the arithmetic of
+ * tk_per_token_cast.  Equal to tk_per_block_cast with block_rows = rows and
+ * block_cols = 1.
+ *
+ *   x, rows, cols, x_ld, q, q_ld, out_dtype, round_pow2, scale_fmt
+ *            as for tk_per_token_cast, with cols any positive multiple of 8.
+ *   scales   float [cols] (16-byte aligned) or int32 [cols/4] (UE8M0, column
+ *            4k+b in byte b of word k; 8-byte aligned).
+ *   workspace  device memory owned by the caller, 16-byte aligned, at least
+ *            tk_per_channel_workspace_bytes(rows, cols) bytes; its contents
+ *            on entry do not matter and are undefined afterwards.  Calls that
+ *            share a workspace must be ordered on one stream.
+ * The cast reads x twice (column maxima, then the codes) in three kernels on
+ * `stream`.  Errors as for tk_per_token_cast; a missing or short workspace
+ * is TK_ERROR_INVALID_VALUE.
+ */
+int64_t tk_per_channel_workspace_bytes(int64_t rows, int64_t cols);
+tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
+                              void *q, int64_t q_ld, void *scales,
+                              void *workspace, int64_t workspace_bytes, int32_t out_dtype,
+                              int32_t round_pow2, int32_t scale_fmt, void *stream);
+
+/*
  * tk_silu32_bf16 -- diagnostic: out[i] = silu32(g[i]) for n bf16 gates, by the
  * same device lookup that tk_swiglu_per_token_cast uses for its gate half
  * (fp32 nearest to g / (1 + e^-g)).  g: bf16 [n] (2-byte aligned), out: fp32

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("tk_per_token_cast", "tk_swiglu_per_token_cast", "tk_status_string", "tk_abi_version",
               "tk_prepare_device", "tk_silu32_bf16", "tk_copy_stream", "tk_per_token_dequant",
-              "tk_per_token_cast_back", "tk_per_token_cast_f32"):
+              "tk_per_token_cast_back", "tk_per_token_cast_f32", "tk_per_block_cast", "tk_per_channel_cast",
+              "tk_per_channel_workspace_bytes"):
         assert n in names
 
 
@@ -157,6 +158,54 @@ def test_cast_f32_validation(kw, want):
     a.update(kw)
     assert tk.tk_per_token_cast_f32(a["x"], a["rows"], a["cols"], a["x_ld"], a["q"], a["q_ld"], a["s"], a["s_ld"],
                                     a["group"], a["out_dtype"], a["round_pow2"], a["scale_fmt"], 0) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(block_cols=48), INVALID), (dict(block_cols=1), INVALID), (dict(block_rows=0), INVALID),
+    (dict(cols=200), INVALID), (dict(out_dtype=2), INVALID), (dict(scale_fmt=2), INVALID),
+    (dict(scale_fmt=1, round_pow2=0), INVALID), (dict(scale_fmt=1, cols=96), INVALID),
+    (dict(x_ld=100), INVALID), (dict(q_ld=100), INVALID), (dict(s_ld=1), INVALID), (dict(rows=-1), INVALID),
+    (dict(x=0), INVALID), (dict(q=0), INVALID), (dict(s=0), INVALID),
+    (dict(x=X + 8), MISALIGNED), (dict(x_ld=260), MISALIGNED), (dict(q=Q + 4), MISALIGNED),
+    (dict(s=S + 2), MISALIGNED), (dict(block_rows=129), UNSUPPORTED), (dict(rows=0, x=0, q=0, s=0), 0),
+])
+def test_per_block_validation(kw, want):
+    a = dict(x=X, rows=4, cols=256, x_ld=256, q=Q, q_ld=256, s=S, s_ld=8, block_rows=128, block_cols=32,
+             out_dtype=0, round_pow2=1, scale_fmt=0)
+    a.update(kw)
+    assert tk.tk_per_block_cast(a["x"], a["rows"], a["cols"], a["x_ld"], a["q"], a["q_ld"], a["s"], a["s_ld"],
+                                a["block_rows"], a["block_cols"], a["out_dtype"], a["round_pow2"], a["scale_fmt"],
+                                0) == want
+
+
+W = 0x50000
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(cols=100), INVALID), (dict(cols=0), INVALID), (dict(rows=-1), INVALID), (dict(out_dtype=2), INVALID),
+    (dict(scale_fmt=1, round_pow2=0), INVALID), (dict(x_ld=100), INVALID), (dict(q_ld=100), INVALID),
+    (dict(x=0), INVALID), (dict(q=0), INVALID), (dict(s=0), INVALID), (dict(ws=0), INVALID),
+    (dict(ws_bytes=16), INVALID), (dict(x=X + 8), MISALIGNED), (dict(q=Q + 4), MISALIGNED),
+    (dict(s=S + 8), MISALIGNED), (dict(ws=W + 8), MISALIGNED),
+    (dict(rows=0, x=0, q=0, s=0, ws=0, ws_bytes=0), 0),
+])
+def test_per_channel_validation(kw, want):
+    a = dict(x=X, rows=4, cols=256, x_ld=256, q=Q, q_ld=256, s=S, ws=W, ws_bytes=None, out_dtype=0, round_pow2=1,
+             scale_fmt=0)
+    a.update(kw)
+    ws_bytes = tk.tk_per_channel_workspace_bytes(a["rows"], a["cols"]) if a["ws_bytes"] is None else a["ws_bytes"]
+    assert tk.tk_per_channel_cast(a["x"], a["rows"], a["cols"], a["x_ld"], a["q"], a["q_ld"], a["s"], a["ws"],
+                                  ws_bytes, a["out_dtype"], a["round_pow2"], a["scale_fmt"], 0) == want
+
+
+def test_per_channel_workspace_size():
+    assert tk.tk_per_channel_workspace_bytes(0, 256) == 0
+    assert tk.tk_per_channel_workspace_bytes(1, 256) == 256 * 2
+    # at most 32 chunks of at least 64 rows
+    assert tk.tk_per_channel_workspace_bytes(64, 256) == 256 * 2
+    assert tk.tk_per_channel_workspace_bytes(65, 256) == 2 * 256 * 2
+    assert tk.tk_per_channel_workspace_bytes(4096, 7168) == 32 * 7168 * 2
+    assert tk.tk_per_channel_workspace_bytes(10**6, 16) <= 32 * 16 * 2
 
 
 def test_copy_stream_validation():
