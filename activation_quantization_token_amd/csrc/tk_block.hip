@@ -4,9 +4,9 @@
 // (include/tk_quant.h) with the |max| taken over a block of rows x channels,
 // or over a whole column.
 //
-// Per-block design.  A workgroup owns one block row (block_rows <= 128 rows)
-// times one stripe of 512 columns.  Each of its waves loads up to 8 rows of
-// the stripe (one 16-byte load, 8 bf16, per lane per row; 1 KiB contiguous
+// Per-block design.  A workgroup owns one block row (block_rows <= 256 rows)
+// times one stripe of 512 columns.  Each of its waves loads RPW = 4, 8 or 16
+// rows of the stripe (one 16-byte load, 8 bf16, per lane per row; 1 KiB contiguous
 // per wave instruction) into registers, reduces |max| over its rows and over
 // the G/8 lanes of each block column with DPP, and the waves combine their
 // maxima through a small LDS table.  The data never leaves registers, so
@@ -17,9 +17,10 @@
 //   1. channel_amax_kernel: workgroups own (row chunk, 512-column stripe)
 //      tiles and write the chunk's column maxima (bf16 magnitude bits) to a
 //      caller-provided workspace [chunks, cols];
-//   2. channel_scale_kernel: the maxima of each column over the chunks ->
-//      scales (written to the output);
-//   3. channel_cast_kernel: every element against its column's scale.  Its
+//   2. channel_cast_kernel: each workgroup first reduces the chunk maxima of
+//      its stripe (all chunk loads in flight at once, then an LDS max across
+//      waves) to the stripe's scales, which one workgroup per stripe also
+//      writes to the output; then it converts its rows against them.  Its
 //      workgroups take the row chunks in reverse order, so the rows the first
 //      pass read last, the ones most likely still in the 256 MB Infinity
 //      Cache, are read first.
@@ -33,9 +34,8 @@
 
 namespace {
 
-constexpr int kBlockRowsPerWave = 8;
-constexpr int kMaxBlockRows = 128;
-constexpr int kMaxBlockWaves = kMaxBlockRows / kBlockRowsPerWave;
+constexpr int kMaxBlockWaves = 16;
+constexpr int kMaxBlockRows = 256;
 
 struct BlockParams {
     const uint16_t *x;   // bf16 bits
@@ -47,9 +47,11 @@ struct BlockParams {
     int64_t block_rows;
 };
 
-template <int BC, int QD, bool POW2, int SF>
+// RPW rows of the block per wave, held in registers (one 16-byte load each).
+template <int BC, int QD, bool POW2, int SF, int RPW>
 __global__ __launch_bounds__(kWave * kMaxBlockWaves) void block_cast_kernel(BlockParams p)
 {
+    constexpr int kBlockRowsPerWave = RPW;
     constexpr int kLanesPerBlock = BC / 8;
     constexpr int kBlocksPerStripe = kSegCols / BC;
     __shared__ uint32_t wave_max[kMaxBlockWaves][kBlocksPerStripe];
@@ -117,15 +119,27 @@ __global__ __launch_bounds__(kWave * kMaxBlockWaves) void block_cast_kernel(Bloc
 // Per-channel cast.
 
 #ifndef TK_CHANNEL_WPB
-#define TK_CHANNEL_WPB 8
+#define TK_CHANNEL_WPB 16
 #endif
 #ifndef TK_CHANNEL_UNROLL
 #define TK_CHANNEL_UNROLL 4
 #endif
 constexpr int kChannelWPB = TK_CHANNEL_WPB;        // waves per workgroup
 constexpr int kChannelUnroll = TK_CHANNEL_UNROLL;  // rows in flight per wave
+#ifndef TK_CHANNEL_REVERSE
+#define TK_CHANNEL_REVERSE 0
+#endif
+constexpr bool kChannelReverse = TK_CHANNEL_REVERSE != 0;
+// The first pass reads x with ordinary (allocating) loads, so that as much of
+// x as the caches hold is still there for the second pass; the second pass
+// reads it non-temporally (its last use).
+#ifndef TK_CHANNEL_P1_POLICY
+#define TK_CHANNEL_P1_POLICY 0
+#endif
+constexpr int kChannelFirstPassPolicy = TK_CHANNEL_P1_POLICY;
 constexpr int64_t kChannelMinChunkRows = 64;
 constexpr int64_t kChannelMaxChunks = 32;
+static_assert(kChannelMaxChunks % kChannelWPB == 0, "each wave reduces the same number of chunks");
 
 struct ChannelParams {
     const uint16_t *x;
@@ -136,6 +150,63 @@ struct ChannelParams {
     uint16_t *ws;          // [chunks, cols] bf16 magnitude bits
     int64_t chunk_rows, chunks;
 };
+
+// Rows [c0, c1) of one 512-column stripe, visited by the waves of a workgroup
+// in batches of U rows per wave (wave w takes rows c0 + w + k W, k < U, of a
+// batch of U W rows).  Each batch's loads are issued before the previous
+// batch is consumed, so U loads per lane are always in flight.
+template <int U, int POLICY = kNonTemporal>
+struct RowBatches {
+    const uint16_t *x;
+    int64_t x_ld, c0, c1;
+    uint32_t row_bytes, byte_off;   // bytes of a row; this lane's offset in it
+    int wave;
+
+    __device__ __forceinline__ int64_t row(int64_t batch, int k) const
+    {
+        return c0 + batch * int64_t(U) * kChannelWPB + int64_t(k) * kChannelWPB + wave;
+    }
+    __device__ __forceinline__ void load(int64_t batch, u32x4 (&w)[U]) const
+    {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t r = row(batch, k);
+            w[k] = u32x4{0u, 0u, 0u, 0u};
+            if (batch >= 0 && r < c1)
+                w[k] = __builtin_amdgcn_raw_buffer_load_b128(row_buffer(x + r * x_ld, row_bytes), int(byte_off), 0,
+                                                             POLICY);
+        }
+    }
+    __device__ __forceinline__ int64_t batches() const
+    {
+        const int64_t per = int64_t(U) * kChannelWPB;
+        return c1 > c0 ? (c1 - c0 + per - 1) / per : 0;
+    }
+};
+
+__device__ __forceinline__ void max_bf16x8(u16x2 (&mx)[4], const u32x4 &w)
+{
+    const u16x2 mag{0x7FFF, 0x7FFF};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx[j] = __builtin_elementwise_max(mx[j], __builtin_bit_cast(u16x2, uint32_t(w[j])) & mag);
+}
+
+// Max of the 8 bf16 magnitudes per lane across the waves of the workgroup
+// (every wave receives the result).  Ends with the LDS table free again.
+__device__ __forceinline__ void workgroup_max(u16x2 (&mx)[4], u32x4 (&part)[kChannelWPB][kWave], int wave, int lane)
+{
+    u32x4 mine;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mine[j] = __builtin_bit_cast(uint32_t, mx[j]);
+    part[wave][lane] = mine;
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < kChannelWPB; ++v) {
+        const u32x4 o = part[v][lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx[j] = __builtin_elementwise_max(mx[j], __builtin_bit_cast(u16x2, uint32_t(o[j])));
+    }
+}
 
 // Pass 1: the |max| of each column over one chunk of rows.
 __global__ __launch_bounds__(kWave * kChannelWPB) void channel_amax_kernel(ChannelParams p)
@@ -150,99 +221,39 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_amax_kernel(Chann
     const int64_t c0 = chunk * p.chunk_rows;
     const int64_t c1 = c0 + p.chunk_rows < p.rows ? c0 + p.chunk_rows : p.rows;
     const uint32_t col = stripe * uint32_t(kSegCols) + uint32_t(lane) * 8u;
+    const RowBatches<kChannelUnroll, kChannelFirstPassPolicy> rb{p.x, p.x_ld, c0, c1, cols * 2u, col * 2u, wave};
     // Running maxima of |x| as bf16 magnitudes, two per word (unsigned
     // 16-bit order is numeric order for them).
     u16x2 mx[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) mx[j] = u16x2{0, 0};
-    const u16x2 mag{0x7FFF, 0x7FFF};
-    for (int64_t r = c0 + wave; r < c1; r += int64_t(kChannelWPB) * kChannelUnroll) {
-        u32x4 w[kChannelUnroll];
+    const int64_t nb = rb.batches();
+    u32x4 w[kChannelUnroll];
+    rb.load(0, w);
+    for (int64_t b = 0; b < nb; ++b) {
+        u32x4 wn[kChannelUnroll];
+        rb.load(b + 1, wn);                 // all-zero past the chunk's end
 #pragma unroll
-        for (int k = 0; k < kChannelUnroll; ++k) {
-            const int64_t row = r + int64_t(k) * kChannelWPB;
-            w[k] = u32x4{0u, 0u, 0u, 0u};
-            if (row < c1) w[k] = load16(row_buffer(p.x + row * p.x_ld, cols * 2u), col * 2u);
-        }
+        for (int k = 0; k < kChannelUnroll; ++k) max_bf16x8(mx, w[k]);
 #pragma unroll
-        for (int k = 0; k < kChannelUnroll; ++k)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                mx[j] = __builtin_elementwise_max(mx[j], __builtin_bit_cast(u16x2, uint32_t(w[k][j])) & mag);
+        for (int k = 0; k < kChannelUnroll; ++k) w[k] = wn[k];
     }
-    u32x4 mine;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mine[j] = __builtin_bit_cast(uint32_t, mx[j]);
-    part[wave][lane] = mine;
-    __syncthreads();
+    workgroup_max(mx, part, wave, lane);
     if (wave == 0) {
-        u16x2 t[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) t[j] = mx[j];
-        for (int v = 1; v < kChannelWPB; ++v) {
-            const u32x4 o = part[v][lane];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) t[j] = __builtin_elementwise_max(t[j], __builtin_bit_cast(u16x2, uint32_t(o[j])));
-        }
         u32x4 out;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[j] = __builtin_bit_cast(uint32_t, t[j]);
+        for (int j = 0; j < 4; ++j) out[j] = __builtin_bit_cast(uint32_t, mx[j]);
         store16(row_buffer(p.ws + chunk * p.cols, cols * 2u), col * 2u, out);
     }
 }
 
-// Pass 2: one thread per 8 columns: the maximum over the chunks -> scales.
-constexpr int kChannelScaleBlock = 256;
-
-template <int QD, bool POW2, int SF>
-__global__ __launch_bounds__(kChannelScaleBlock) void channel_scale_kernel(ChannelParams p)
-{
-    const int64_t t = int64_t(blockIdx.x) * kChannelScaleBlock + threadIdx.x;
-    const uint32_t cols = uint32_t(p.cols);
-    const uint32_t col = uint32_t(t) * 8u;
-    if (col >= cols) return;
-    u16x2 mx[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mx[j] = u16x2{0, 0};
-    for (int64_t c = 0; c < p.chunks; ++c) {
-        const u32x4 w = load16(row_buffer(p.ws + c * p.cols, cols * 2u), col * 2u);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx[j] = __builtin_elementwise_max(mx[j], __builtin_bit_cast(u16x2, uint32_t(w[j])));
-    }
-    float s[8];
-    uint32_t e8[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t amax_bits = uint32_t(h ? mx[j].y : mx[j].x) << 16;
-            const Scale<QD, POW2> sc = group_scale<QD, POW2>(amax_bits);
-            s[2 * j + h] = sc.s;
-            e8[2 * j + h] = sc.e8;
-        }
-    }
-    if constexpr (SF == kScaleF32) {
-        const __amdgpu_buffer_rsrc_t srow = row_buffer(p.s, cols * 4u);
-        u32x4 a, b;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            a[i] = __float_as_uint(s[i]);
-            b[i] = __float_as_uint(s[4 + i]);
-        }
-        __builtin_amdgcn_raw_buffer_store_b128(a, srow, int(col * 4u), 0, TK_SCALE_STORE_POLICY);
-        __builtin_amdgcn_raw_buffer_store_b128(b, srow, int(col * 4u + 16u), 0, TK_SCALE_STORE_POLICY);
-    } else {
-        const __amdgpu_buffer_rsrc_t srow = row_buffer(p.s, cols);
-        const u32x2 v{e8[0] | (e8[1] << 8) | (e8[2] << 16) | (e8[3] << 24),
-                      e8[4] | (e8[5] << 8) | (e8[6] << 16) | (e8[7] << 24)};
-        __builtin_amdgcn_raw_buffer_store_b64(v, srow, int(col), 0, TK_SCALE_STORE_POLICY);
-    }
-}
-
-// Pass 3: codes against the column scales, row chunks in reverse order.
+// Pass 2: the stripe's scales from the chunk maxima, then codes against the
+// column scales.  The first batch of rows is loaded before the chunk maxima
+// are reduced, so their latencies overlap.
 template <int QD, bool POW2, int SF>
 __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(ChannelParams p)
 {
+    __shared__ u32x4 part[kChannelWPB][kWave];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t cols = uint32_t(p.cols);
@@ -252,40 +263,67 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(Chann
     const int64_t c0 = chunk * p.chunk_rows;
     const int64_t c1 = c0 + p.chunk_rows < p.rows ? c0 + p.chunk_rows : p.rows;
     const uint32_t col = stripe * uint32_t(kSegCols) + uint32_t(lane) * 8u;
-    // This lane's 8 column scales (and, for powers of two, their exact
-    // reciprocals), read back from the scale output.
+    const RowBatches<kChannelUnroll> rb{p.x, p.x_ld, c0, c1, cols * 2u, col * 2u, wave};
+    const int64_t nb = rb.batches();
+    // Batch order: descending when kChannelReverse, so that the rows the
+    // first pass read last (the likeliest still cached) come first.
+    auto batch_at = [&](int64_t i) { return kChannelReverse ? nb - 1 - i : i; };
+    u32x4 w[kChannelUnroll];
+    rb.load(batch_at(0), w);
+
+    // Column maxima of this lane's 8 columns over every chunk: wave w takes
+    // chunks w, w + W, ... (all its loads issued before any is used).
+    constexpr int kChunkLoads = int(kChannelMaxChunks) / kChannelWPB;
+    u32x4 cw[kChunkLoads];
+#pragma unroll
+    for (int k = 0; k < kChunkLoads; ++k) {
+        const int64_t c = wave + int64_t(k) * kChannelWPB;
+        cw[k] = u32x4{0u, 0u, 0u, 0u};
+        if (c < p.chunks) cw[k] = load16(row_buffer(p.ws + c * p.cols, cols * 2u), col * 2u);
+    }
+    u16x2 mx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx[j] = u16x2{0, 0};
+#pragma unroll
+    for (int k = 0; k < kChunkLoads; ++k) max_bf16x8(mx, cw[k]);
+    workgroup_max(mx, part, wave, lane);
+
     float s[8], inv[8];
-    if constexpr (SF == kScaleF32) {
-        const __amdgpu_buffer_rsrc_t srow = row_buffer(p.s, cols * 4u);
-        const u32x4 a = load16(srow, col * 4u), b = load16(srow, col * 4u + 16u);
+    uint32_t e8[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s[i] = __uint_as_float(a[i]);
-            s[4 + i] = __uint_as_float(b[i]);
-        }
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t amax_bits = uint32_t((i & 1) ? mx[i / 2].y : mx[i / 2].x) << 16;
+        const Scale<QD, POW2> sc = group_scale<QD, POW2>(amax_bits);
+        s[i] = sc.s;
+        inv[i] = sc.inv;
+        e8[i] = sc.e8;
+    }
+    if (blockIdx.x < stripes && wave == 0) {      // one workgroup per stripe
+        if constexpr (SF == kScaleF32) {
+            const __amdgpu_buffer_rsrc_t srow = row_buffer(p.s, cols * 4u);
+            u32x4 a, b;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) inv[i] = __uint_as_float(0x7F000000u - (__float_as_uint(s[i]) & 0x7F800000u));
-    } else {
-        const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(row_buffer(p.s, cols), int(col), 0, 0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t E = (e[i / 4] >> (8 * (i % 4))) & 0xFFu;
-            s[i] = __uint_as_float(E << 23);
-            inv[i] = __uint_as_float((254u - E) << 23);
+            for (int i = 0; i < 4; ++i) {
+                a[i] = __float_as_uint(s[i]);
+                b[i] = __float_as_uint(s[4 + i]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(a, srow, int(col * 4u), 0, TK_SCALE_STORE_POLICY);
+            __builtin_amdgcn_raw_buffer_store_b128(b, srow, int(col * 4u + 16u), 0, TK_SCALE_STORE_POLICY);
+        } else {
+            const __amdgpu_buffer_rsrc_t srow = row_buffer(p.s, cols);
+            const u32x2 v{e8[0] | (e8[1] << 8) | (e8[2] << 16) | (e8[3] << 24),
+                          e8[4] | (e8[5] << 8) | (e8[6] << 16) | (e8[7] << 24)};
+            __builtin_amdgcn_raw_buffer_store_b64(v, srow, int(col), 0, TK_SCALE_STORE_POLICY);
         }
     }
+
     const uint32_t qbytes = QD == kE4M3 ? cols : cols / 2;
-    for (int64_t r = c0 + wave; r < c1; r += int64_t(kChannelWPB) * kChannelUnroll) {
-        u32x4 w[kChannelUnroll];
+    for (int64_t i = 0; i < nb; ++i) {
+        u32x4 wn[kChannelUnroll];
+        rb.load(batch_at(i + 1), wn);       // nothing past the last batch
 #pragma unroll
         for (int k = 0; k < kChannelUnroll; ++k) {
-            const int64_t row = r + int64_t(k) * kChannelWPB;
-            w[k] = u32x4{0u, 0u, 0u, 0u};
-            if (row < c1) w[k] = load16(row_buffer(p.x + row * p.x_ld, cols * 2u), col * 2u);
-        }
-#pragma unroll
-        for (int k = 0; k < kChannelUnroll; ++k) {
-            const int64_t row = r + int64_t(k) * kChannelWPB;
+            const int64_t row = rb.row(batch_at(i), k);
             if (row < c1) {
                 float x[8], v[8];
                 widen8(w[k], x);
@@ -297,6 +335,8 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(Chann
                 else store4(qrow, col / 2, codes.x);
             }
         }
+#pragma unroll
+        for (int k = 0; k < kChannelUnroll; ++k) w[k] = wn[k];
     }
 }
 
@@ -307,36 +347,52 @@ using BlockFn = void (*)(BlockParams);
 using ChannelFn = void (*)(ChannelParams);
 
 struct BlockTable {
-    BlockFn fn[4][2][3];         // [block_cols index][code format][variant]
+    BlockFn fn[3][4][2][3];      // [rows per wave 4/8/16][block_cols index][code format][variant]
 };
 struct ChannelTable {
-    ChannelFn scale[2][3], cast[2][3];   // [code format][variant]
+    ChannelFn cast[2][3];        // [code format][variant]
 };
 
-template <int BC, int QD>
-void fill_block(BlockFn (&t)[3])
+template <int BC, int QD, int RPW>
+void fill_block_rpw(BlockFn (&t)[3])
 {
-    t[0] = block_cast_kernel<BC, QD, false, kScaleF32>;
-    t[1] = block_cast_kernel<BC, QD, true, kScaleF32>;
-    t[2] = block_cast_kernel<BC, QD, true, kScaleUE8M0>;
+    t[0] = block_cast_kernel<BC, QD, false, kScaleF32, RPW>;
+    t[1] = block_cast_kernel<BC, QD, true, kScaleF32, RPW>;
+    t[2] = block_cast_kernel<BC, QD, true, kScaleUE8M0, RPW>;
+}
+
+template <int BC, int QD>
+void fill_block(BlockTable &t, int bci)
+{
+    fill_block_rpw<BC, QD, 4>(t.fn[0][bci][QD]);
+    fill_block_rpw<BC, QD, 8>(t.fn[1][bci][QD]);
+    fill_block_rpw<BC, QD, 16>(t.fn[2][bci][QD]);
 }
 
 BlockTable make_block_table()
 {
     BlockTable t;
-    fill_block<16, kE4M3>(t.fn[0][0]);  fill_block<16, kE2M1>(t.fn[0][1]);
-    fill_block<32, kE4M3>(t.fn[1][0]);  fill_block<32, kE2M1>(t.fn[1][1]);
-    fill_block<64, kE4M3>(t.fn[2][0]);  fill_block<64, kE2M1>(t.fn[2][1]);
-    fill_block<128, kE4M3>(t.fn[3][0]); fill_block<128, kE2M1>(t.fn[3][1]);
+    fill_block<16, kE4M3>(t, 0);  fill_block<16, kE2M1>(t, 0);
+    fill_block<32, kE4M3>(t, 1);  fill_block<32, kE2M1>(t, 1);
+    fill_block<64, kE4M3>(t, 2);  fill_block<64, kE2M1>(t, 2);
+    fill_block<128, kE4M3>(t, 3); fill_block<128, kE2M1>(t, 3);
     return t;
+}
+
+// Rows per wave for a launch (measured on MI355X over bf16 [32768, 7168] and
+// [4096, 7168]): 4 up to 32-row blocks, 8 up to 64, and for 128-row blocks
+// 16 once there are at least 8 tiles per CU (8 below: fewer, shorter waves
+// finish a small grid sooner); 16 above 128 rows.
+int block_rpw_index(int64_t block_rows, int64_t tiles, int cus)
+{
+    if (block_rows > 128) return 2;
+    if (block_rows > 64) return tiles >= 8 * int64_t(cus) ? 2 : 1;
+    return block_rows > 32 ? 1 : 0;
 }
 
 template <int QD>
 void fill_channel(ChannelTable &t)
 {
-    t.scale[QD][0] = channel_scale_kernel<QD, false, kScaleF32>;
-    t.scale[QD][1] = channel_scale_kernel<QD, true, kScaleF32>;
-    t.scale[QD][2] = channel_scale_kernel<QD, true, kScaleUE8M0>;
     t.cast[QD][0] = channel_cast_kernel<QD, false, kScaleF32>;
     t.cast[QD][1] = channel_cast_kernel<QD, true, kScaleF32>;
     t.cast[QD][2] = channel_cast_kernel<QD, true, kScaleUE8M0>;
@@ -402,6 +458,10 @@ tk_status tk_per_block_cast(const void *x, int64_t rows, int64_t cols, int64_t x
     if (st != TK_SUCCESS || rows == 0) return st;
     if (block_rows > kMaxBlockRows) return TK_ERROR_UNSUPPORTED;
     if (!aligned(scales, 4)) return TK_ERROR_MISALIGNED;
+    // Blocks of one row are the per-token groups: same layouts, same values.
+    if (block_rows == 1)
+        return tk_per_token_cast(x, rows, cols, x_ld, q, q_ld, scales, s_ld, int32_t(block_cols), out_dtype,
+                                 round_pow2, scale_fmt, stream);
     int dev = 0;
     DeviceInfo *info = nullptr;
     st = device_info(&dev, &info);
@@ -412,14 +472,17 @@ tk_status tk_per_block_cast(const void *x, int64_t rows, int64_t cols, int64_t x
     const int64_t stripes = (cols + kSegCols - 1) / kSegCols;
     const int64_t blocks = nbr * stripes;
     if (blocks > int64_t(0x7FFFFFFF)) return TK_ERROR_UNSUPPORTED;
+    const int ri = block_rpw_index(block_rows, blocks, info->cus);
+    const int64_t rpw = int64_t(4) << ri;
     const int64_t used_rows = block_rows < rows ? block_rows : rows;
-    const int waves = int((used_rows + kBlockRowsPerWave - 1) / kBlockRowsPerWave);
+    const int waves = int((used_rows + rpw - 1) / rpw);     // <= kMaxBlockWaves
     BlockParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld, scales, s_ld,
                   block_rows};
+    const int bci = block_cols_index(block_cols);
+    hipStream_t s = static_cast<hipStream_t>(stream);
     void *args[] = {&p};
-    const BlockFn fn = table.fn[block_cols_index(block_cols)][out_dtype][variant];
-    if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * waves), args, 0,
-                        static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (hipLaunchKernel(reinterpret_cast<const void *>(table.fn[ri][bci][out_dtype][variant]), dim3(uint32_t(blocks)),
+                        dim3(kWave * waves), args, 0, s) != hipSuccess)
         return TK_ERROR_LAUNCH;
     return TK_SUCCESS;
 }
@@ -455,10 +518,6 @@ tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t
     void *args[] = {&p};
     if (hipLaunchKernel(reinterpret_cast<const void *>(channel_amax_kernel), dim3(uint32_t(tiles)),
                         dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
-        return TK_ERROR_LAUNCH;
-    const int64_t scale_blocks = (cols / 8 + kChannelScaleBlock - 1) / kChannelScaleBlock;
-    if (hipLaunchKernel(reinterpret_cast<const void *>(table.scale[out_dtype][variant]), dim3(uint32_t(scale_blocks)),
-                        dim3(kChannelScaleBlock), args, 0, s) != hipSuccess)
         return TK_ERROR_LAUNCH;
     if (hipLaunchKernel(reinterpret_cast<const void *>(table.cast[out_dtype][variant]), dim3(uint32_t(tiles)),
                         dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)

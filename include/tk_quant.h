@@ -180,7 +180,7 @@ tk_status tk_per_token_cast_back(const void *x, int64_t rows, int64_t cols, int6
  *            [ceil(rows/block_rows), cols/block_cols/4] (UE8M0, four blocks of
  *            one block row per int32, block 4k+b in byte b); row stride s_ld
  *            elements.
- *   block_rows  1 .. 128 (larger: TK_ERROR_UNSUPPORTED).
+ *   block_rows  1 .. 256 (larger: TK_ERROR_UNSUPPORTED); 1 is the per-token cast.
  *   block_cols  16, 32, 64 or 128.
  * Alignment and errors as for tk_per_token_cast.
  */
@@ -204,7 +204,7 @@ tk_status tk_per_block_cast(const void *x, int64_t rows, int64_t cols, int64_t x
  *            tk_per_channel_workspace_bytes(rows, cols) bytes; its contents
  *            on entry do not matter and are undefined afterwards.  Calls that
  *            share a workspace must be ordered on one stream.
- * The cast reads x twice (column maxima, then the codes) in three kernels on
+ * The cast reads x twice (column maxima, then the codes) in two kernels on
  * `stream`.  Errors as for tk_per_token_cast; a missing or short workspace
  * is TK_ERROR_INVALID_VALUE.
  */

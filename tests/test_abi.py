@@ -167,7 +167,7 @@ def test_cast_f32_validation(kw, want):
     (dict(x_ld=100), INVALID), (dict(q_ld=100), INVALID), (dict(s_ld=1), INVALID), (dict(rows=-1), INVALID),
     (dict(x=0), INVALID), (dict(q=0), INVALID), (dict(s=0), INVALID),
     (dict(x=X + 8), MISALIGNED), (dict(x_ld=260), MISALIGNED), (dict(q=Q + 4), MISALIGNED),
-    (dict(s=S + 2), MISALIGNED), (dict(block_rows=129), UNSUPPORTED), (dict(rows=0, x=0, q=0, s=0), 0),
+    (dict(s=S + 2), MISALIGNED), (dict(block_rows=257), UNSUPPORTED), (dict(rows=0, x=0, q=0, s=0), 0),
 ])
 def test_per_block_validation(kw, want):
     a = dict(x=X, rows=4, cols=256, x_ld=256, q=Q, q_ld=256, s=S, s_ld=8, block_rows=128, block_cols=32,

@@ -85,7 +85,8 @@ def check_channel(x_bits, dt, p2, sf, x_ld=None, workspace=None, label=""):
 
 # (rows, block_rows, extra columns beyond whole 512-column stripes in units of
 # 4 blocks): partial last block rows, odd block heights, ragged last stripes.
-BLOCK_SHAPES = [(1, 128, 0), (130, 128, 1), (40, 13, 1), (67, 8, 0), (33, 1, 1), (200, 64, 2)]
+BLOCK_SHAPES = [(1, 128, 0), (130, 128, 1), (40, 13, 1), (67, 8, 0), (33, 1, 1), (200, 64, 2), (300, 200, 1),
+                (520, 256, 0)]
 
 
 @pytest.mark.parametrize("dt,p2,sf", VARIANTS)
@@ -103,6 +104,13 @@ def test_per_block_full_size(dt, p2, sf, br, bc):
     w = inputs.WORKLOADS[1]
     x = inputs.generate(w, cache=True)
     check_block(x, br, bc, dt, p2, sf, label="4096x7168")
+
+
+def test_per_block_largest_workload_128x128():
+    """bf16 [32768, 7168]: enough tiles for the 16-rows-per-wave launch."""
+    w = inputs.WORKLOADS[4]
+    x = inputs.generate(w, cache=True)
+    check_block(x, 128, 128, "e4m3", True, "ue8m0", label="32768x7168")
 
 
 def test_per_block_of_one_row_equals_per_token():
