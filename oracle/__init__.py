@@ -8,9 +8,12 @@ The arithmetic lives in ``tk_oracle.c`` (plain scalar C, one IEEE binary32
 operation per step); this module builds it with gcc, loads it with ctypes and
 offers numpy-array wrappers.  The definition it follows, step by step, is
 written out at the top of ``tk_oracle.c`` with its sources on the pages:
-"Tile Kernels" (PyPI, v2.0.0) Features; "TileKernels" (aiwiki.ai) section
-Quantization; "TileKernels, TileLang kernels for MoE routing and low-precision
-quantization" (hysenlabs.com) section "Seven kernel families".
+"Tile Kernels" (PyPI, v2.0.0) Features; "TileKernels" (aiwiki.ai) sections
+Quantization and Version 2.0.0; "TileKernels, TileLang kernels for MoE routing
+and low-precision quantization" (hysenlabs.com) section "Seven kernel
+families".  Besides the per-token cast it covers the fused SwiGLU form,
+dequantization, cast-and-cast-back, fp32 input, the per-block and per-channel
+casts, and RMSNorm forward with the optional fused cast.
 """
 from __future__ import annotations
 
@@ -73,6 +76,12 @@ def _open(path) -> ctypes.CDLL:
     lib.oracle_per_token_cast_back.restype = ctypes.c_int
     lib.oracle_per_block_cast.argtypes = [p, i64, i64, i64, p, i64, p, i64, i64, i64, i32, i32, i32]
     lib.oracle_per_block_cast.restype = ctypes.c_int
+    lib.oracle_rmsnorm.argtypes = [p, i64, i64, i64, p, ctypes.c_float, p, i64, i32, p]
+    lib.oracle_rmsnorm.restype = ctypes.c_int
+    lib.oracle_rmsnorm_cast.argtypes = [p, i64, i64, i64, p, ctypes.c_float, p, i64, p, i64, i32, i32, i32, i32, p]
+    lib.oracle_rmsnorm_cast.restype = ctypes.c_int
+    lib.oracle_sum_squares_rows.argtypes = [p, i64, i64, i64, p]
+    lib.oracle_sum_squares_rows.restype = None
     lib.oracle_code_value_n.argtypes = [p, p, i64, i32]
     lib.oracle_code_value_n.restype = None
     lib.oracle_f32_to_bf16_n.argtypes = [p, p, i64]
@@ -308,3 +317,52 @@ def per_channel_cast(x: np.ndarray, out_dtype: str = "e4m3", round_pow2: bool = 
     rows = x.shape[0]
     q, s = per_block_cast(x, max(rows, 1), 1, out_dtype, round_pow2, scale_fmt)
     return q, s.reshape(-1)
+
+
+def sum_squares(x: np.ndarray) -> np.ndarray:
+    """Per row of bf16 bits x: the exact sum of squares rounded to fp32."""
+    _check_2d(x)
+    out = np.empty(x.shape[0], dtype=np.float32)
+    _lib().oracle_sum_squares_rows(_ptr(x), x.shape[0], x.shape[1], x.strides[0] // 2, _ptr(out))
+    return out
+
+
+def _weight_ptr(weight, cols):
+    if weight is None:
+        return None, None
+    w = np.ascontiguousarray(weight, dtype=np.uint16)
+    if w.shape != (cols,):
+        raise ValueError("weight must be bf16 bits of shape [cols]")
+    return w, _ptr(w)
+
+
+def rmsnorm(x: np.ndarray, weight: np.ndarray | None = None, eps: float = 1e-6, out: str = "bf16") -> np.ndarray:
+    """Oracle RMSNorm forward of bf16 bits x [rows, cols] with bf16 weight bits
+    [cols] (or none) -> bf16 bits (uint16) or fp32 [rows, cols]."""
+    _check_2d(x)
+    rows, cols = x.shape
+    w, wp = _weight_ptr(weight, cols)
+    y = np.empty((rows, cols), dtype=np.uint16 if out == "bf16" else np.float32)
+    work = np.empty(cols, dtype=np.float32)
+    rc = _lib().oracle_rmsnorm(_ptr(x), rows, cols, x.strides[0] // 2, wp, eps, _ptr(y), cols,
+                               0 if out == "bf16" else 1, _ptr(work))
+    if rc != 0:
+        raise ValueError("oracle rejected the RMSNorm arguments")
+    return y
+
+
+def rmsnorm_cast(x: np.ndarray, weight: np.ndarray | None = None, eps: float = 1e-6, group: int = 128,
+                 out_dtype: str = "e4m3", round_pow2: bool = False, scale_fmt: str = "f32"):
+    """Oracle RMSNorm forward followed by the per-token cast of its fp32
+    output -> (codes, scales) as per_token_cast returns them."""
+    _check_2d(x)
+    rows, cols = x.shape
+    w, wp = _weight_ptr(weight, cols)
+    q, s = _outputs(rows, cols, group, out_dtype, scale_fmt)
+    work = np.empty(cols, dtype=np.float32)
+    rc = _lib().oracle_rmsnorm_cast(_ptr(x), rows, cols, x.strides[0] // 2, wp, eps, _ptr(q), q.shape[1],
+                                    _ptr(s), s.shape[1], group, _QDTYPES[out_dtype], int(bool(round_pow2)),
+                                    _SCALE_FMTS[scale_fmt], _ptr(work))
+    if rc != 0:
+        raise ValueError("oracle rejected the RMSNorm-cast arguments")
+    return q, s

@@ -36,11 +36,16 @@
  * dequantization") maps a code back to y = fl32(value(code) * s), returned as
  * fp32 or rounded to bf16 (nearest, ties to even); the per-token
  * cast-and-cast-back ("TileKernels" (aiwiki.ai), Version 2.0.0) is the cast
- * above followed by that dequantization, bf16 out.
+ * above followed by that dequantization, bf16 out.  The per-block and
+ * per-channel casts ("Tile Kernels" (PyPI, v2.0.0), Features) take step 1
+ * over a block of rows x channels or over a whole column.  RMSNorm forward
+ * with the optional fused cast ("TileKernels" (aiwiki.ai), Version 2.0.0) is
+ * defined where it is implemented below.
  * Every float operation below is one IEEE binary32 operation rounded to
  * nearest-even; build with -O2 -ffp-contract=off and without fast-math.
  * Results for NaN or Inf inputs are outside the contract.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -405,6 +410,136 @@ int oracle_per_token_cast_back(const uint16_t *x, int64_t rows, int64_t cols, in
             return -1;
     }
     return 0;
+}
+
+/* ---- RMSNorm forward, alone and followed by the per-token cast -------- */
+
+/* "TileKernels" (aiwiki.ai), Version 2.0.0: RMSNorm forward, with an
+ * optional fused FP8 cast.  The pages name the operation only; this is the
+ * textbook root-mean-square normalisation of a row of C values with a
+ * per-channel weight w (bf16, or none = all ones) and eps > 0:
+ *   ss  = sum_j x_j^2, the exact sum rounded once to fp32 (nearest-even);
+ *   t   = fl32(ss / C);  t = fl32(t + eps);
+ *   r   = fl32(1 / fl32(sqrt(t)));
+ *   y_j = fl32(x_j * r), then y_j = fl32(y_j * w_j) with a weight.
+ * The fused form casts y per token exactly as the cast above casts fp32
+ * activations. */
+
+/* A little-endian multiword integer of 32-bit words holding sum_j x_j^2 *
+ * 2^266: a nonzero bf16 value is M * 2^k (M < 2^8, k >= -133), so x^2 =
+ * M^2 * 2^(2k) with 2k + 266 >= 0; the largest, 2k + 266 <= 506 plus 16 bits
+ * of M^2, leaves room for 2^40 terms below 18 * 32 bits. */
+#define SQ_WORDS 18
+#define SQ_SHIFT 266
+
+static void sq_add(uint32_t *acc, uint16_t b)
+{
+    uint32_t e = (b >> 7) & 0xFFu, m = b & 0x7Fu;
+    if (e == 0 && m == 0) return;
+    int k = (e == 0) ? -133 : (int)e - 134;          /* value = M * 2^k */
+    uint32_t M = (e == 0) ? m : (m | 0x80u);
+    int p = 2 * k + SQ_SHIFT;                        /* bit position of M^2 */
+    uint64_t v = (uint64_t)(M * M) << (p % 32);
+    int w = p / 32;
+    uint64_t carry = 0;
+    for (int i = w; i < SQ_WORDS; ++i) {
+        uint64_t add = (i == w) ? (v & 0xFFFFFFFFu) : (i == w + 1) ? (v >> 32) : 0;
+        uint64_t t = (uint64_t)acc[i] + add + carry;
+        acc[i] = (uint32_t)t;
+        carry = t >> 32;
+        if (carry == 0 && i > w) break;
+    }
+}
+
+static int sq_bit(const uint32_t *acc, int i)
+{
+    return (int)((acc[i / 32] >> (i % 32)) & 1u);
+}
+
+/* The multiword value * 2^-266 rounded to fp32, nearest with ties to even
+ * (subnormal results rounded at 2^-149; overflow gives +Inf). */
+static float sq_round_f32(const uint32_t *acc)
+{
+    int top = -1;
+    for (int i = SQ_WORDS * 32 - 1; i >= 0; --i)
+        if (sq_bit(acc, i)) { top = i; break; }
+    if (top < 0) return 0.0f;
+    int lsb = top - 23;
+    if (lsb < SQ_SHIFT - 149) lsb = SQ_SHIFT - 149;
+    uint64_t mant = 0;
+    for (int i = top; i >= lsb; --i) mant = (mant << 1) | (uint64_t)sq_bit(acc, i);
+    int round = (lsb >= 1) ? sq_bit(acc, lsb - 1) : 0;
+    int sticky = 0;
+    for (int i = lsb - 2; i >= 0 && !sticky; --i) sticky = sq_bit(acc, i);
+    if (round && (sticky || (mant & 1u))) mant += 1;
+    double v = ldexp((double)mant, lsb - SQ_SHIFT);   /* exact: mant <= 2^24 */
+    if (v > (double)FLT_MAX) return INFINITY;
+    return (float)v;
+}
+
+float oracle_sum_squares_f32(const uint16_t *x, int64_t n)
+{
+    uint32_t acc[SQ_WORDS];
+    memset(acc, 0, sizeof(acc));
+    for (int64_t j = 0; j < n; ++j) sq_add(acc, x[j]);
+    return sq_round_f32(acc);
+}
+
+static void rmsnorm_row(const uint16_t *x, int64_t cols, const uint16_t *w, float eps, float *y)
+{
+    float ss = oracle_sum_squares_f32(x, cols);
+    float t = ss / (float)cols;
+    t = t + eps;
+    float rs = sqrtf(t);
+    float r = 1.0f / rs;
+    for (int64_t j = 0; j < cols; ++j) {
+        float v = bf16_to_f32(x[j]) * r;
+        y[j] = w ? v * bf16_to_f32(w[j]) : v;
+    }
+}
+
+static int valid_rmsnorm(int64_t rows, int64_t cols, float eps)
+{
+    return rows >= 0 && cols > 0 && cols < (1 << 24) && eps > 0.0f && isfinite(eps);
+}
+
+/* x: bf16 bits [rows, cols] (row stride x_ld); w: bf16 bits [cols] or NULL;
+ * y: [rows, cols] with row stride y_ld, bf16 bits (y_dtype 0, nearest-even
+ * from the fp32 y) or fp32 (y_dtype 1).  Returns 0 or -1 (bad arguments). */
+int oracle_rmsnorm(const uint16_t *x, int64_t rows, int64_t cols, int64_t x_ld, const uint16_t *w, float eps,
+                   void *y, int64_t y_ld, int32_t y_dtype, float *work /* cols floats */)
+{
+    if (!valid_rmsnorm(rows, cols, eps) || (y_dtype != 0 && y_dtype != 1)) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        rmsnorm_row(x + r * x_ld, cols, w, eps, work);
+        for (int64_t c = 0; c < cols; ++c) {
+            if (y_dtype == 1) ((float *)y)[r * y_ld + c] = work[c];
+            else ((uint16_t *)y)[r * y_ld + c] = f32_to_bf16_rne(work[c]);
+        }
+    }
+    return 0;
+}
+
+/* RMSNorm followed by the per-token cast of the fp32 y; outputs as in
+ * oracle_per_token_cast. */
+int oracle_rmsnorm_cast(const uint16_t *x, int64_t rows, int64_t cols, int64_t x_ld, const uint16_t *w, float eps,
+                        uint8_t *q, int64_t q_ld, void *scales, int64_t s_ld, int32_t group, int32_t qdtype,
+                        int32_t round_pow2, int32_t scale_fmt, float *work /* cols floats */)
+{
+    if (!valid_rmsnorm(rows, cols, eps)) return -1;
+    if (!valid_common(rows, cols, group, qdtype, round_pow2, scale_fmt)) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        rmsnorm_row(x + r * x_ld, cols, w, eps, work);
+        void *srow = (scale_fmt == ORACLE_SCALE_F32) ? (void *)((float *)scales + r * s_ld)
+                                                     : (void *)((uint32_t *)scales + r * s_ld);
+        cast_row(work, cols, q + r * q_ld, srow, group, qdtype, round_pow2, scale_fmt);
+    }
+    return 0;
+}
+
+void oracle_sum_squares_rows(const uint16_t *x, int64_t rows, int64_t cols, int64_t x_ld, float *out)
+{
+    for (int64_t r = 0; r < rows; ++r) out[r] = oracle_sum_squares_f32(x + r * x_ld, cols);
 }
 
 /* ---- array forms of the single steps, for the pin tests -------------- */

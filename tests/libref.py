@@ -198,3 +198,35 @@ def block_cast_values(x: np.ndarray, block_rows: int, block_cols: int, out_dtype
 
 def per_block_cast(x_bits, block_rows=128, block_cols=128, out_dtype="e4m3", round_pow2=False, scale_fmt="f32"):
     return block_cast_values(widen(x_bits), block_rows, block_cols, out_dtype, round_pow2, scale_fmt)
+
+
+def sum_squares_exact_f32(x_bits: np.ndarray) -> np.ndarray:
+    """Per row: the exact sum of squares (Python integers on the bf16 values'
+    integer significands) rounded to binary32 by tests/exact.py."""
+    from exact import round_to_f32
+    out = np.empty(x_bits.shape[0], dtype=np.float32)
+    for r in range(x_bits.shape[0]):
+        total = Fraction(0)
+        for v in widen(x_bits[r]).astype(np.float64):
+            if v != 0.0:
+                total += Fraction(float(v)) ** 2
+        try:
+            out[r] = round_to_f32(total)
+        except OverflowError:
+            out[r] = np.inf
+    return out
+
+
+def rmsnorm(x_bits: np.ndarray, w_bits, eps: float, ss: np.ndarray | None = None) -> np.ndarray:
+    """RMSNorm forward as numpy float32 operations (IEEE, nearest-even) on the
+    exactly rounded sum of squares: fp32 y [rows, cols]."""
+    rows, cols = x_bits.shape
+    ss = sum_squares_exact_f32(x_bits) if ss is None else ss
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        t = (ss / np.float32(cols)).astype(np.float32)
+        t = (t + np.float32(eps)).astype(np.float32)
+        r = (np.float32(1.0) / np.sqrt(t)).astype(np.float32)
+        y = (widen(x_bits) * r[:, None]).astype(np.float32)
+        if w_bits is not None:
+            y = (y * widen(np.asarray(w_bits))[None, :]).astype(np.float32)
+    return y

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import test_oracle_block_pins as bpins
+import test_oracle_rmsnorm_pins as rpins
 import test_oracle_dequant_pins as dpins
 import test_oracle_pins as pins
 
@@ -57,6 +58,16 @@ MUTATIONS = [
     ("block UE8M0 big-endian", "<< (8 * (bj % 4))", "<< (8 * (3 - bj % 4))", None),
     ("block amax over one column", "for (int64_t c = c0; c < c0 + block_cols; ++c) {\n                    float a",
      "for (int64_t c = c0; c < c0 + 1; ++c) {\n                    float a", None),
+    ("sum of squares in fp32", "for (int64_t j = 0; j < n; ++j) sq_add(acc, x[j]);\n    return sq_round_f32(acc);",
+     "float f = 0.0f;\n    for (int64_t j = 0; j < n; ++j) f += bf16_to_f32(x[j]) * bf16_to_f32(x[j]);\n"
+     "    (void)sq_add; (void)sq_round_f32;\n    return f;", None),
+    ("sum of squares rounds ties up", "if (round && (sticky || (mant & 1u))) mant += 1;", "if (round) mant += 1;", None),
+    ("sum of squares without subnormal rounding", "if (lsb < SQ_SHIFT - 149) lsb = SQ_SHIFT - 149;", "", None),
+    ("eps added before the mean", "float t = ss / (float)cols;\n    t = t + eps;",
+     "float t = (ss + eps) / (float)cols;", None),
+    ("rsqrt rounded once", "float rs = sqrtf(t);\n    float r = 1.0f / rs;",
+     "float r = (float)(1.0 / sqrt((double)t));", None),
+    ("weight ignored", "y[j] = w ? v * bf16_to_f32(w[j]) : v;", "y[j] = v; (void)w;", None),
     ("decode drops the sign", "return (float)((code & 0x80) ? -m : m);", "return (float)m;", None),
 ]
 
@@ -72,6 +83,10 @@ def _checks():
             lambda: dpins.test_dequant_vs_library_composition(128, "e4m3", "f32", False, "f32"),
             lambda: dpins.test_cast_back_vs_library_composition(64, "e4m3", True),
             lambda: bpins.test_per_block_vs_library_composition("e4m3", True, "ue8m0", 32, 32, 37),
+            lambda: [rpins.test_sum_squares_rounding_cases(v, e) for v, e in rpins.MIDPOINT_ROWS],
+            lambda: rpins.test_sum_squares_exact("wide"),
+            lambda: rpins.test_rmsnorm_vs_library_composition(True, 1e-6),
+            lambda: rpins.test_rmsnorm_vs_library_composition(False, 0.5),
             lambda: bpins.test_per_block_vs_library_composition("e2m1", False, "f32", 16, 64, 37),
             lambda: pins.test_whole_tensor_vs_library_composition(32, "e2m1", True, "ue8m0", 3, 4),
             lambda: pins.test_whole_tensor_division_hard_cases("e4m3"),
