@@ -18,6 +18,8 @@ from .binding import (  # noqa: F401
     per_token_cast,
     per_token_cast_back,
     per_token_dequant,
+    rmsnorm,
+    rmsnorm_cast,
     silu32_bf16,
     swiglu_per_token_cast,
     tk_abi_version,
@@ -30,6 +32,8 @@ from .binding import (  # noqa: F401
     tk_per_token_cast_back,
     tk_per_token_dequant,
     tk_prepare_device,
+    tk_rmsnorm,
+    tk_rmsnorm_cast,
     tk_silu32_bf16,
     tk_status_string,
     tk_swiglu_per_token_cast,

@@ -63,6 +63,11 @@ def load_library(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
         lib.tk_per_channel_workspace_bytes.restype = i64
         lib.tk_per_channel_cast.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, i64, i32, i32, i32, vp]
         lib.tk_per_channel_cast.restype = ctypes.c_int
+        f32 = ctypes.c_float
+        lib.tk_rmsnorm.argtypes = [vp, i64, i64, i64, vp, f32, vp, i64, i32, vp]
+        lib.tk_rmsnorm.restype = ctypes.c_int
+        lib.tk_rmsnorm_cast.argtypes = [vp, i64, i64, i64, vp, f32, vp, i64, vp, i64, i32, i32, i32, i32, vp]
+        lib.tk_rmsnorm_cast.restype = ctypes.c_int
         lib.tk_silu32_bf16.argtypes = [vp, vp, i64, vp]
         lib.tk_silu32_bf16.restype = ctypes.c_int
         lib.tk_copy_stream.argtypes = [vp, vp, i64, vp]
@@ -357,3 +362,51 @@ def per_channel_cast(x: torch.Tensor, out_dtype: str = "e4m3", round_pow2: bool 
                                workspace.data_ptr(), ws_bytes, QDTYPES[out_dtype], int(bool(round_pow2)),
                                SCALE_FMTS[scale_fmt], _stream_handle(stream, x.device)))
     return q, s
+
+
+def tk_rmsnorm(x: int, rows: int, cols: int, x_ld: int, weight: int | None, eps: float, y: int, y_ld: int,
+               y_dtype: int, stream: int) -> int:
+    """Raw C call with integer pointers; returns the tk_status code."""
+    return load_library().tk_rmsnorm(x, rows, cols, x_ld, weight, eps, y, y_ld, y_dtype, stream)
+
+
+def tk_rmsnorm_cast(x: int, rows: int, cols: int, x_ld: int, weight: int | None, eps: float, q: int, q_ld: int,
+                    scales: int, s_ld: int, group: int, out_dtype: int, round_pow2: int, scale_fmt: int,
+                    stream: int) -> int:
+    """Raw C call with integer pointers; returns the tk_status code."""
+    return load_library().tk_rmsnorm_cast(x, rows, cols, x_ld, weight, eps, q, q_ld, scales, s_ld, group, out_dtype,
+                                          round_pow2, scale_fmt, stream)
+
+
+def _weight(weight, x):
+    if weight is None:
+        return None
+    if (not isinstance(weight, torch.Tensor) or weight.dtype != torch.bfloat16 or weight.dim() != 1
+            or weight.shape[0] != x.shape[1] or not weight.is_contiguous() or weight.device != x.device):
+        raise TypeError("weight must be a contiguous 1-D bf16 tensor of x.shape[1] on x's device")
+    return weight.data_ptr()
+
+
+def rmsnorm(x: torch.Tensor, weight: torch.Tensor | None = None, eps: float = 1e-6, out_dtype: str = "bf16",
+            out=None, stream=None) -> torch.Tensor:
+    """RMSNorm forward of bf16 x [rows, cols] -> y in bf16 or fp32."""
+    _check_input(x, "x")
+    rows, cols = x.shape
+    ydt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    y = torch.empty((rows, cols), dtype=ydt, device=x.device) if out is None else out
+    if y.dtype != ydt or y.dim() != 2 or y.stride(1) != 1 or tuple(y.shape) != (rows, cols) or y.device != x.device:
+        raise ValueError("out must be a row-contiguous tensor of x's shape and the output dtype")
+    _check(tk_rmsnorm(x.data_ptr(), rows, cols, x.stride(0), _weight(weight, x), float(eps), y.data_ptr(),
+                      y.stride(0), OUT_DTYPES[out_dtype], _stream_handle(stream, x.device)))
+    return y
+
+
+def rmsnorm_cast(x: torch.Tensor, weight: torch.Tensor | None = None, eps: float = 1e-6, group: int = 128,
+                 out_dtype: str = "e4m3", round_pow2: bool = False, scale_fmt: str = "f32", out=None, stream=None):
+    """RMSNorm forward fused with the per-token cast -> (codes, scales)."""
+    _check_input(x, "x")
+    wp = _weight(weight, x)
+
+    def fn(xp, rows, cols, x_ld, q, q_ld, s, s_ld, g, dt, p2, sf, st):
+        return tk_rmsnorm_cast(xp, rows, cols, x_ld, wp, float(eps), q, q_ld, s, s_ld, g, dt, p2, sf, st)
+    return _run(fn, x, x.shape[1], group, out_dtype, round_pow2, scale_fmt, out, stream)

@@ -1,0 +1,647 @@
+// tk_norm.hip -- gfx950 kernels and C ABI for RMSNorm forward, alone and
+// with the per-token cast fused after it ("TileKernels" (aiwiki.ai), Version
+// 2.0.0: RMSNorm forward with an optional fused FP8 cast).  The arithmetic
+// contract is written out in include/tk_quant.h.
+//
+// Design.  The fused cast of rows of up to 7168 channels runs one row per
+// wave (see rmsnorm_wave_kernel below).  Otherwise a workgroup owns one row
+// at a time (a persistent grid strides over the rows, each workgroup prefetching
+// its next row) and holds the whole row in registers: W = ceil(cols / 1024) waves, each lane 2
+// segments of 8 bf16 (16-byte loads, 1 KiB per wave instruction), so rows of
+// up to 16384 channels are read from memory exactly once.  The weight row is
+// loaded once per workgroup into the same lane layout.
+//
+// The sum of squares is defined as the exact sum rounded once to fp32.  Each
+// lane sums its squares in fp64 (a bf16 square is exact in fp64), the waves
+// reduce with cross-lane shuffles and through LDS in a fixed order, and the
+// fp64 result D is certified: the exact sum differs from D by at most 37
+// roundings of 2^-53 relative (16 per lane, 6 shuffle levels, up to 15 wave
+// sums), well inside D * 2^-46, so when D +- D * 2^-46 lies strictly between
+// the two fp32 rounding midpoints around fl32(D), fl32(D) is the answer.
+// Otherwise (about one row in 2^20 for random data; also every row whose
+// exact sum sits on a midpoint, and sums outside the fp32 normal range) the
+// workgroup recomputes the sum exactly with an integer accumulator in LDS and
+// rounds it by hand.  Wave 0 alone turns the wave sums into r and hands it to
+// the other waves through LDS.
+
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <stdint.h>
+
+#include "tk_device.h"
+#include "tk_host.h"
+
+namespace {
+
+constexpr int kNormU = 2;                         // segments per lane
+constexpr int kNormMaxWaves = 16;
+constexpr int64_t kNormMaxCols = int64_t(kNormMaxWaves) * kNormU * kSegCols;   // 16384
+constexpr int kExactDigits = 18;                  // 32-bit digits of the exact accumulator
+constexpr int kExactShift = 266;                  // x^2 * 2^266 is an integer for every bf16 x
+
+enum { kOutCast = 0, kOutBF16 = 1, kOutF32 = 2 };
+
+struct NormParams {
+    const uint16_t *x;
+    int64_t rows, cols, x_ld;
+    const uint16_t *w;    // bf16 [cols] or null
+    float eps;
+    void *out;            // codes, or y
+    int64_t out_ld;       // bytes (codes) or elements (y)
+    void *s;
+    int64_t s_ld;
+};
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int mask, int lane)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = shfl_u32(uint32_t(b), lane ^ mask), hi = shfl_u32(uint32_t(b >> 32), lane ^ mask);
+    return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+// True when fl32(D) is certainly the exact sum S rounded to fp32, given
+// |S - D| <= D * 2^-46 (S, D >= 0).  That bound is at most 128 units in the
+// last place of D's fp64 binade, and the fp32 rounding midpoints in that
+// binade are exactly the values whose 29 low mantissa bits (the ones fl32
+// drops) read 2^28.  So fl32(D) is safe unless those bits lie within 256 of
+// 2^28; D outside the fp32 normal range (below 2^-126, or from 2^127 up,
+// where fl32 may overflow) is left to the exact path too.
+__device__ __forceinline__ bool certified(double d)
+{
+    if (d == 0.0) return true;                    // all squares zero: exact
+    const uint64_t b = __builtin_bit_cast(uint64_t, d);
+    const uint32_t e = uint32_t(b >> 52);         // biased exponent, d > 0
+    if (e < 1023u - 126u || e >= 1023u + 127u) return false;
+    const uint32_t dropped = uint32_t(b) & 0x1FFFFFFFu;
+    const uint32_t half = 0x10000000u;
+    const uint32_t dist = dropped > half ? dropped - half : half - dropped;
+    return dist > 256u;
+}
+
+// Exact sum of squares of the row, rounded to fp32 by hand: integer digits
+// in LDS (64-bit atomic adds of 32-bit pieces, carries resolved at the end by
+// one thread).  Called by every thread of the workgroup.
+__device__ float exact_sum_squares(const u32x4 (&w)[kNormU], unsigned long long *acc, float *result)
+{
+    if (threadIdx.x < kExactDigits) acc[threadIdx.x] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kNormU; ++k) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t b = (w[k][i / 2] >> (16 * (i % 2))) & 0x7FFFu;
+            const uint32_t e = b >> 7, m = b & 0x7Fu;
+            if (b != 0u) {
+                const int kexp = e ? int(e) - 134 : -133;      // |x| = M * 2^kexp
+                const uint32_t M = e ? (m | 0x80u) : m;
+                const int p = 2 * kexp + kExactShift;           // >= 0
+                const uint64_t v = uint64_t(M * M) << (p & 31);
+                atomicAdd(&acc[p >> 5], (unsigned long long)(v & 0xFFFFFFFFull));
+                atomicAdd(&acc[(p >> 5) + 1], (unsigned long long)(v >> 32));
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t dig[kExactDigits];
+        uint64_t carry = 0;
+        for (int i = 0; i < kExactDigits; ++i) {
+            const uint64_t t = acc[i] + carry;
+            dig[i] = uint32_t(t);
+            carry = t >> 32;
+        }
+        int top = -1;
+        for (int i = kExactDigits - 1; i >= 0 && top < 0; --i)
+            if (dig[i]) top = i * 32 + 31 - __builtin_clz(dig[i]);
+        float r = 0.0f;
+        if (top >= 0) {
+            int lsb = top - 23;
+            if (lsb < kExactShift - 149) lsb = kExactShift - 149;     // fp32 subnormal spacing
+            auto bit = [&](int i) -> uint32_t { return (dig[i >> 5] >> (i & 31)) & 1u; };
+            uint64_t mant = 0;
+            for (int i = top; i >= lsb; --i) mant = (mant << 1) | bit(i);
+            const uint32_t round = lsb >= 1 ? bit(lsb - 1) : 0u;
+            uint32_t sticky = 0;
+            for (int i = lsb - 2; i >= 0 && !sticky; --i) sticky = bit(i);
+            if (round && (sticky || (mant & 1u))) mant += 1;
+            const double v = __builtin_ldexp(double(mant), lsb - kExactShift);   // exact
+            r = v > double(FLT_MAX) ? __builtin_inff() : float(v);
+        }
+        *result = r;
+    }
+    __syncthreads();
+    return *result;
+}
+
+// r = fl32(1 / fl32(sqrt(fl32(fl32(ss / C) + eps)))): IEEE fp32 division
+// and square root (HIP's defaults: correctly rounded), one rounding per step.
+__device__ __forceinline__ float inv_rms(float ss, float cols_f, float eps)
+{
+    const float t = ss / cols_f + eps;
+    return 1.0f / __builtin_sqrtf(t);
+}
+
+// Sum over the wave of an fp64 value, every lane receiving the same result:
+// four DPP steps within each 16-lane row (lane ^ 1, lane ^ 2, then the
+// half-row and row mirrors), then two cross-row shuffles.  Each step adds two
+// partners' identical-order sums, so all lanes stay bit-identical.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = dpp_mov<CTRL>(uint32_t(b)), hi = dpp_mov<CTRL>(uint32_t(b >> 32));
+    return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v, int lane)
+{
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x141>(v);
+    v += dpp_f64<0x140>(v);
+    v += shfl_xor_f64(v, 16, lane);
+    v += shfl_xor_f64(v, 32, lane);
+    return v;
+}
+
+// Persistent form: a workgroup takes rows blockIdx.x, blockIdx.x + gridDim.x,
+// ... and loads its next row before it reduces the current one, so a row's
+// load latency overlaps the previous row's reduction, barrier and stores.
+#ifndef TK_NORM_WAVES_PER_EU
+#define TK_NORM_WAVES_PER_EU 1
+#endif
+#ifndef TK_NORM_PACKED_WEIGHT
+#define TK_NORM_PACKED_WEIGHT 0
+#endif
+template <int G, int QD, bool POW2, int SF, int OUT>
+__global__ __launch_bounds__(kWave * kNormMaxWaves) __attribute__((amdgpu_waves_per_eu(TK_NORM_WAVES_PER_EU)))
+void rmsnorm_kernel(NormParams p)
+{
+    extern __shared__ uint32_t row_scales[];      // the row's scale words (cast form)
+    __shared__ double wave_sum[kNormMaxWaves];
+    __shared__ unsigned long long exact_acc[kExactDigits];
+    __shared__ float exact_result;
+    __shared__ float row_r;
+    __shared__ int row_exact;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = int(blockDim.x) >> 6;
+    const uint32_t cols = uint32_t(p.cols);
+    const uint32_t col0 = uint32_t(wave) * uint32_t(kNormU * kSegCols) + uint32_t(lane) * 8u;
+    const float cols_f = float(p.cols);           // exact: cols < 2^24
+
+    // weight row in the x layout, kept as packed bf16 (zeros past the row
+    // end); without a weight every factor is 1.0, and x * r * 1 = x * r.
+    u32x4 wt[kNormU];
+#pragma unroll
+    for (int k = 0; k < kNormU; ++k) wt[k] = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    if (p.w) {
+        const __amdgpu_buffer_rsrc_t wrow = row_buffer(p.w, cols * 2u);
+#pragma unroll
+        for (int k = 0; k < kNormU; ++k)
+            wt[k] = __builtin_amdgcn_raw_buffer_load_b128(wrow, int((col0 + k * kSegCols) * 2u), 0, 0);
+    }
+
+    auto load_row = [&](int64_t row, u32x4 (&w)[kNormU]) {
+        const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + row * p.x_ld, cols * 2u);
+#pragma unroll
+        for (int k = 0; k < kNormU; ++k) w[k] = load16(xrow, (col0 + k * kSegCols) * 2u);
+    };
+
+    int64_t row = blockIdx.x;
+    u32x4 w[kNormU];
+    if (row < p.rows) load_row(row, w);
+    for (; row < p.rows; row += gridDim.x) {
+#if TK_NORM_PACKED_WEIGHT
+        // keep the weight packed (8 registers) instead of letting the
+        // compiler hoist its widened form (16) out of the loop
+#pragma unroll
+        for (int k = 0; k < kNormU; ++k) asm volatile("" : "+v"(wt[k]));
+#endif
+        u32x4 wn[kNormU];
+        const int64_t next = row + gridDim.x;
+#pragma unroll
+        for (int k = 0; k < kNormU; ++k) wn[k] = u32x4{0u, 0u, 0u, 0u};
+        if (next < p.rows) load_row(next, wn);
+
+        // fp64 sum of squares: per lane, across the wave, across the waves
+        double acc = 0.0;
+#pragma unroll
+        for (int k = 0; k < kNormU; ++k) {
+            float x[8];
+            widen8(w[k], x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc = __builtin_fma(double(x[i]), double(x[i]), acc);
+        }
+        acc = wave_sum_f64(acc, lane);
+        if (lane == 0) wave_sum[wave] = acc;
+        __syncthreads();
+        if (wave == 0) {
+            double d = 0.0;
+            for (int v = 0; v < nw; ++v) d += wave_sum[v];
+            const bool ok = certified(d);
+            const float r0 = ok ? inv_rms(float(d), cols_f, p.eps) : 0.0f;
+            if (lane == 0) {
+                row_r = r0;
+                row_exact = ok ? 0 : 1;
+            }
+        }
+        __syncthreads();
+        float r;
+        if (row_exact) r = inv_rms(exact_sum_squares(w, exact_acc, &exact_result), cols_f, p.eps);   // uniform
+        else r = row_r;
+
+        if constexpr (OUT == kOutCast) {
+            constexpr int kLanesPerGroup = G / 8;
+            const uint32_t s_words = SF == kScaleF32 ? cols / G : cols / G / 4;
+            const __amdgpu_buffer_rsrc_t qrow =
+                row_buffer(static_cast<uint8_t *>(p.out) + row * p.out_ld, QD == kE4M3 ? cols : cols / 2);
+#pragma unroll
+            for (int k = 0; k < kNormU; ++k) {
+                const uint32_t col = col0 + k * kSegCols;
+                float x[8], wf[8], y[8];
+                widen8(w[k], x);
+                widen8(wt[k], wf);
+                uint32_t amax = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    y[i] = (x[i] * r) * wf[i];
+                    amax = max(amax, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+                }
+                const Quantized qz = quantize_segment<G, QD, POW2>(y, amax);
+                if constexpr (QD == kE4M3) store8(qrow, col, qz.codes);
+                else store4(qrow, col / 2, qz.codes.x);
+                if constexpr (SF == kScaleF32) {
+                    if ((lane % kLanesPerGroup) == 0 && col < cols) row_scales[col / G] = __float_as_uint(qz.s);
+                } else {
+                    const uint32_t word = pack_e8_word<G>(qz.e8, lane);
+                    if ((lane % (4 * kLanesPerGroup)) == 0 && col < cols) row_scales[col / (4 * G)] = word;
+                }
+            }
+            __syncthreads();
+            __amdgpu_buffer_rsrc_t srow;
+            if constexpr (SF == kScaleF32) srow = row_buffer(static_cast<float *>(p.s) + row * p.s_ld, s_words * 4u);
+            else srow = row_buffer(static_cast<uint32_t *>(p.s) + row * p.s_ld, s_words * 4u);
+            for (uint32_t t2 = threadIdx.x; t2 < s_words; t2 += blockDim.x) store_scale(srow, t2 * 4u, row_scales[t2]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kNormU; ++k) {
+                const uint32_t col = col0 + k * kSegCols;
+                float x[8], wf[8], y[8];
+                widen8(w[k], x);
+                widen8(wt[k], wf);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = (x[i] * r) * wf[i];
+                if constexpr (OUT == kOutBF16) {
+                    const __amdgpu_buffer_rsrc_t yrow =
+                        row_buffer(static_cast<uint16_t *>(p.out) + row * p.out_ld, cols * 2u);
+                    store16(yrow, col * 2u, pack_bf16x8(y));
+                } else {
+                    const __amdgpu_buffer_rsrc_t yrow =
+                        row_buffer(static_cast<float *>(p.out) + row * p.out_ld, cols * 4u);
+                    u32x4 a, b;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        a[i] = __float_as_uint(y[i]);
+                        b[i] = __float_as_uint(y[4 + i]);
+                    }
+                    store16(yrow, col * 4u, a);
+                    store16(yrow, col * 4u + 16u, b);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kNormU; ++k) w[k] = wn[k];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One wave per row, for rows of up to 7168 channels.  Each wave of a 4-wave
+// workgroup runs its own row loop (rows wave_id, wave_id + total waves, ...):
+// the row's NS 512-column segments stay in registers, the sum of squares needs
+// only the in-wave reduction, the per-row scalar work (certification,
+// division, square root, reciprocal) is spread over 8 NS values per lane, and
+// no workgroup barrier is taken inside the loop.  The weight row is staged
+// once per workgroup in LDS as fp32 (zeros past the row end); each wave
+// gathers its row's scale words in its own LDS slice and writes them with one
+// coalesced store per 256 bytes.  Segments past the row end load zeros and
+// store nothing (buffer bounds), so NS only has to cover the row.  A lane sums
+// up to 8 NS = 112 squares in sequence: with the 6 shuffle levels that is at
+// most 118 roundings, within the 256-unit margin of certified().
+
+constexpr int kNormWaveWPB = 4;
+
+// Exact sum of squares of one wave's row (its lanes' NS segments), rounded
+// to fp32; the arithmetic of exact_sum_squares, with the digits in this
+// wave's own LDS slice and no workgroup barrier (a wave's LDS operations take
+// effect in program order).
+template <int NS>
+__device__ float exact_sum_squares_wave(const u32x4 (&xs)[NS], unsigned long long *acc, int lane)
+{
+    if (lane < kExactDigits) acc[lane] = 0ull;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t b = (xs[k][i / 2] >> (16 * (i % 2))) & 0x7FFFu;
+            const uint32_t e = b >> 7, m = b & 0x7Fu;
+            if (b != 0u) {
+                const int kexp = e ? int(e) - 134 : -133;
+                const uint32_t M = e ? (m | 0x80u) : m;
+                const int pos = 2 * kexp + kExactShift;
+                const uint64_t v = uint64_t(M * M) << (pos & 31);
+                atomicAdd(&acc[pos >> 5], (unsigned long long)(v & 0xFFFFFFFFull));
+                atomicAdd(&acc[(pos >> 5) + 1], (unsigned long long)(v >> 32));
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    uint32_t result = 0;
+    if (lane == 0) {
+        uint32_t dig[kExactDigits];
+        uint64_t carry = 0;
+        for (int i = 0; i < kExactDigits; ++i) {
+            const uint64_t t = acc[i] + carry;
+            dig[i] = uint32_t(t);
+            carry = t >> 32;
+        }
+        int top = -1;
+        for (int i = kExactDigits - 1; i >= 0 && top < 0; --i)
+            if (dig[i]) top = i * 32 + 31 - __builtin_clz(dig[i]);
+        float r = 0.0f;
+        if (top >= 0) {
+            int lsb = top - 23;
+            if (lsb < kExactShift - 149) lsb = kExactShift - 149;
+            auto bit = [&](int i) -> uint32_t { return (dig[i >> 5] >> (i & 31)) & 1u; };
+            uint64_t mant = 0;
+            for (int i = top; i >= lsb; --i) mant = (mant << 1) | bit(i);
+            const uint32_t round = lsb >= 1 ? bit(lsb - 1) : 0u;
+            uint32_t sticky = 0;
+            for (int i = lsb - 2; i >= 0 && !sticky; --i) sticky = bit(i);
+            if (round && (sticky || (mant & 1u))) mant += 1;
+            const double v = __builtin_ldexp(double(mant), lsb - kExactShift);
+            r = v > double(FLT_MAX) ? __builtin_inff() : float(v);
+        }
+        result = __float_as_uint(r);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    return __uint_as_float(__builtin_amdgcn_readfirstlane(result));
+}
+
+// 8 consecutive fp32 weights from LDS (col a multiple of 8: two 16-byte reads)
+__device__ __forceinline__ void weight8(const float *w, uint32_t col, float (&wf)[8])
+{
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(w + col), b = *reinterpret_cast<const f32x4 *>(w + col + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        wf[i] = a[i];
+        wf[4 + i] = b[i];
+    }
+}
+
+template <int G, int QD, bool POW2, int SF, int OUT, int NS>
+__global__ __launch_bounds__(kWave * kNormWaveWPB) void rmsnorm_wave_kernel(NormParams p)
+{
+    static_assert(OUT == kOutCast, "the one-wave-per-row kernel serves the fused cast");
+    constexpr int kCols = NS * kSegCols;
+    extern __shared__ float lds_weight[];                                 // fp32 [NS * 512]
+    __shared__ uint32_t stage[kNormWaveWPB][kCols / 16];
+    __shared__ unsigned long long exact_acc[kNormWaveWPB][kExactDigits];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t cols = uint32_t(p.cols);
+    const float cols_f = float(p.cols);
+
+    // weight row into LDS as fp32: w_j, 1.0 without a weight, 0 past the row
+    for (uint32_t t = threadIdx.x; t < uint32_t(kCols); t += blockDim.x)
+        lds_weight[t] = t < cols ? (p.w ? __uint_as_float(uint32_t(p.w[t]) << 16) : 1.0f) : 0.0f;
+    __syncthreads();                              // the only workgroup barrier
+
+    const int64_t nwaves = int64_t(gridDim.x) * kNormWaveWPB;
+    for (int64_t row_it = int64_t(blockIdx.x) * kNormWaveWPB + wave; row_it < p.rows; row_it += nwaves) {
+        // the row is the same on every lane; saying so keeps the row
+        // descriptors in scalar registers
+        const int64_t row = int64_t(uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(row_it >> 32)))) << 32 |
+                                    uint32_t(__builtin_amdgcn_readfirstlane(int(row_it))));
+        // segment k of this lane: byte lane * 16 + k * 1024 of the row, the
+        // segment offset in the instruction's scalar offset
+        const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + row * p.x_ld, cols * 2u);
+        u32x4 xs[NS];
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+            xs[k] = __builtin_amdgcn_raw_buffer_load_b128(xrow, int(lane * 16), k * kSegCols * 2, kNonTemporal);
+        double acc = 0.0;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            float x[8];
+            widen8(xs[k], x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc = __builtin_fma(double(x[i]), double(x[i]), acc);
+        }
+        // the widened values are recomputed below rather than kept alive
+        // across the reduction (8 registers per segment instead of 4)
+#pragma unroll
+        for (int k = 0; k < NS; ++k) asm volatile("" : "+v"(xs[k]));
+        const double d = wave_sum_f64(acc, lane);
+        const float ss = certified(d) ? float(d) : exact_sum_squares_wave<NS>(xs, exact_acc[wave], lane);
+        const float r = inv_rms(ss, cols_f, p.eps);
+
+        {
+            constexpr int kLanesPerGroup = G / 8;
+            const uint32_t s_words = SF == kScaleF32 ? cols / G : cols / G / 4;
+            const __amdgpu_buffer_rsrc_t qrow =
+                row_buffer(static_cast<uint8_t *>(p.out) + row * p.out_ld, QD == kE4M3 ? cols : cols / 2);
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                const uint32_t col = uint32_t(k) * kSegCols + uint32_t(lane) * 8u;
+                float x[8], y[8], wf[8];
+                widen8(xs[k], x);
+                weight8(lds_weight, col, wf);
+                uint32_t amax = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    y[i] = (x[i] * r) * wf[i];
+                    amax = max(amax, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+                }
+                const Quantized qz = quantize_segment<G, QD, POW2>(y, amax);
+                if constexpr (QD == kE4M3)
+                    __builtin_amdgcn_raw_buffer_store_b64(qz.codes, qrow, int(lane * 8), k * kSegCols, kNonTemporal);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(qz.codes.x, qrow, int(lane * 4), k * kSegCols / 2,
+                                                          kNonTemporal);
+                if constexpr (SF == kScaleF32) {
+                    if ((lane % kLanesPerGroup) == 0 && col < cols) stage[wave][col / G] = __float_as_uint(qz.s);
+                } else {
+                    const uint32_t word = pack_e8_word<G>(qz.e8, lane);
+                    if ((lane % (4 * kLanesPerGroup)) == 0 && col < cols) stage[wave][col / (4 * G)] = word;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __amdgpu_buffer_rsrc_t srow;
+            if constexpr (SF == kScaleF32) srow = row_buffer(static_cast<float *>(p.s) + row * p.s_ld, s_words * 4u);
+            else srow = row_buffer(static_cast<uint32_t *>(p.s) + row * p.s_ld, s_words * 4u);
+            for (uint32_t t = uint32_t(lane); t < s_words; t += kWave) store_scale(srow, t * 4u, stage[wave][t]);
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
+    }
+}
+
+using NormFn = void (*)(NormParams);
+
+// One-wave-per-row variants by segments held per lane: 4 (rows up to 2048
+// channels), 8 (up to 4096), 14 (up to 7168); wider rows take the
+// workgroup-per-row kernel.
+constexpr int kWaveNS[3] = {4, 8, 14};
+
+struct NormTable {
+    NormFn cast[4][4][2][3];     // [kernel: workgroup, NS 4/8/14][group][code format][variant]
+    NormFn plain[2];             // [bf16 y, fp32 y], workgroup-per-row kernel
+};
+
+template <int G, int QD, bool POW2, int SF>
+void fill_norm_variant(NormTable &t, int gi, int vi)
+{
+    t.cast[0][gi][QD][vi] = rmsnorm_kernel<G, QD, POW2, SF, kOutCast>;
+    t.cast[1][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 4>;
+    t.cast[2][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 8>;
+    t.cast[3][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 14>;
+}
+
+template <int G, int QD>
+void fill_norm(NormTable &t, int gi)
+{
+    fill_norm_variant<G, QD, false, kScaleF32>(t, gi, 0);
+    fill_norm_variant<G, QD, true, kScaleF32>(t, gi, 1);
+    fill_norm_variant<G, QD, true, kScaleUE8M0>(t, gi, 2);
+}
+
+
+NormTable make_norm_table()
+{
+    NormTable t;
+    fill_norm<16, kE4M3>(t, 0);  fill_norm<16, kE2M1>(t, 0);
+    fill_norm<32, kE4M3>(t, 1);  fill_norm<32, kE2M1>(t, 1);
+    fill_norm<64, kE4M3>(t, 2);  fill_norm<64, kE2M1>(t, 2);
+    fill_norm<128, kE4M3>(t, 3); fill_norm<128, kE2M1>(t, 3);
+    t.plain[0] = rmsnorm_kernel<16, kE4M3, false, kScaleF32, kOutBF16>;
+    t.plain[1] = rmsnorm_kernel<16, kE4M3, false, kScaleF32, kOutF32>;
+    return t;
+}
+
+tk_status validate_norm(const void *x, int64_t rows, int64_t cols, int64_t x_ld, const void *weight, float eps)
+{
+    if (rows < 0 || cols <= 0 || x_ld < cols) return TK_ERROR_INVALID_VALUE;
+    if (!(eps > 0.0f) || !(eps <= FLT_MAX)) return TK_ERROR_INVALID_VALUE;
+    if (cols > kNormMaxCols) return TK_ERROR_UNSUPPORTED;
+    if (rows == 0) return TK_SUCCESS;
+    if (!x) return TK_ERROR_INVALID_VALUE;
+    if (!aligned(x, 16) || (x_ld * 2) % 16 != 0 || (weight && !aligned(weight, 16))) return TK_ERROR_MISALIGNED;
+    return TK_SUCCESS;
+}
+
+// Resident waves aimed for per CU by the persistent grids.
+#ifndef TK_NORM_WAVES_PER_CU
+#define TK_NORM_WAVES_PER_CU 32
+#endif
+#ifndef TK_NORM_WAVE_WAVES_PER_CU
+#define TK_NORM_WAVE_WAVES_PER_CU 16
+#endif
+
+// 0: workgroup-per-row kernel; 1..3: one wave per row holding 4/8/14 segments.
+int norm_kernel_index(int64_t cols)
+{
+    for (int i = 0; i < 3; ++i)
+        if (cols <= int64_t(kWaveNS[i]) * kSegCols) return i + 1;
+    return 0;
+}
+
+tk_status launch_norm(const NormTable &t, int gi, int qd, int variant, int plain, const NormParams &p, int64_t s_words,
+                      int cus, hipStream_t s)
+{
+    NormParams q = p;
+    void *args[] = {&q};
+    // The plain forward (y written) measured faster with the workgroup-per-row
+    // kernel at every width; the fused cast with one wave per row.
+    const int ki = plain >= 0 ? 0 : norm_kernel_index(p.cols);
+    const NormFn fn = plain >= 0 ? t.plain[plain] : t.cast[ki][gi][qd][variant];
+    if (ki > 0) {
+        int64_t blocks = int64_t(cus) * (TK_NORM_WAVE_WAVES_PER_CU / kNormWaveWPB);
+        const int64_t need = (p.rows + kNormWaveWPB - 1) / kNormWaveWPB;
+        if (blocks > need) blocks = need;
+        const size_t lds = size_t(kWaveNS[ki - 1]) * kSegCols * 4u;      // fp32 weight row
+        if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * kNormWaveWPB),
+                            args, lds, s) != hipSuccess)
+            return TK_ERROR_LAUNCH;
+        return TK_SUCCESS;
+    }
+    const int waves = int((p.cols + kNormU * kSegCols - 1) / (kNormU * kSegCols));
+    int64_t per_cu = TK_NORM_WAVES_PER_CU / waves;
+    if (per_cu < 1) per_cu = 1;
+    int64_t blocks = int64_t(cus) * per_cu;
+    if (blocks > p.rows) blocks = p.rows;
+    if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * waves), args,
+                        size_t(s_words * 4), s) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    return TK_SUCCESS;
+}
+
+int norm_group_index(int32_t g) { return g == 16 ? 0 : g == 32 ? 1 : g == 64 ? 2 : 3; }
+
+}  // namespace
+
+extern "C" {
+
+tk_status tk_rmsnorm(const void *x, int64_t rows, int64_t cols, int64_t x_ld, const void *weight, float eps, void *y,
+                     int64_t y_ld, int32_t y_dtype, void *stream)
+{
+    if (y_dtype != TK_OUT_BF16 && y_dtype != TK_OUT_F32) return TK_ERROR_INVALID_VALUE;
+    if (cols <= 0 || cols % 8 != 0 || y_ld < cols) return TK_ERROR_INVALID_VALUE;
+    tk_status st = validate_norm(x, rows, cols, x_ld, weight, eps);
+    if (st != TK_SUCCESS || rows == 0) return st;
+    if (!y) return TK_ERROR_INVALID_VALUE;
+    const int64_t ysize = y_dtype == TK_OUT_F32 ? 4 : 2;
+    if (!aligned(y, 16) || (y_ld * ysize) % 16 != 0) return TK_ERROR_MISALIGNED;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    st = device_info(&dev, &info);
+    if (st != TK_SUCCESS) return st;
+    static const NormTable table = make_norm_table();
+    NormParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<const uint16_t *>(weight), eps, y,
+                 y_ld, nullptr, 0};
+    return launch_norm(table, 0, 0, 0, y_dtype == TK_OUT_F32 ? 1 : 0, p, 0, info->cus, static_cast<hipStream_t>(stream));
+}
+
+tk_status tk_rmsnorm_cast(const void *x, int64_t rows, int64_t cols, int64_t x_ld, const void *weight, float eps,
+                          void *q, int64_t q_ld, void *scales, int64_t s_ld, int32_t group, int32_t out_dtype,
+                          int32_t round_pow2, int32_t scale_fmt, void *stream)
+{
+    if (group != 16 && group != 32 && group != 64 && group != 128) return TK_ERROR_INVALID_VALUE;
+    if (out_dtype != kE4M3 && out_dtype != kE2M1) return TK_ERROR_INVALID_VALUE;
+    if (scale_fmt != kScaleF32 && scale_fmt != kScaleUE8M0) return TK_ERROR_INVALID_VALUE;
+    if (cols <= 0 || cols % group != 0) return TK_ERROR_INVALID_VALUE;
+    const int64_t ngroups = cols / group;
+    if (scale_fmt == kScaleUE8M0 && (!round_pow2 || ngroups % 4 != 0)) return TK_ERROR_INVALID_VALUE;
+    const int64_t q_cols = out_dtype == kE4M3 ? cols : cols / 2;
+    const int64_t s_cols = scale_fmt == kScaleF32 ? ngroups : ngroups / 4;
+    if (q_ld < q_cols || s_ld < s_cols) return TK_ERROR_INVALID_VALUE;
+    tk_status st = validate_norm(x, rows, cols, x_ld, weight, eps);
+    if (st != TK_SUCCESS || rows == 0) return st;
+    if (!q || !scales) return TK_ERROR_INVALID_VALUE;
+    const int64_t qa = out_dtype == kE4M3 ? 8 : 4;
+    if (!aligned(q, uintptr_t(qa)) || q_ld % qa != 0 || !aligned(scales, 4)) return TK_ERROR_MISALIGNED;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    st = device_info(&dev, &info);
+    if (st != TK_SUCCESS) return st;
+    static const NormTable table = make_norm_table();
+    const int variant = !round_pow2 ? 0 : (scale_fmt == kScaleF32 ? 1 : 2);
+    NormParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<const uint16_t *>(weight), eps, q,
+                 q_ld, scales, s_ld};
+    return launch_norm(table, norm_group_index(group), out_dtype, variant, -1, p, s_cols, info->cus,
+                       static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -136,10 +136,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed steps; HBM and fabric clocks need ~15 ms of sustained load to settle")
     ap.add_argument("--workload", type=int, default=4)
-    ap.add_argument("--op", choices=["cast", "dequant", "cast_back", "per_block", "per_channel"], default="cast",
+    ap.add_argument("--op", choices=["cast", "dequant", "cast_back", "per_block", "per_channel", "rmsnorm", "rmsnorm_cast"], default="cast",
                     help="cast (the workload's cast, fused SwiGLU for workload 3), its dequantization, "
-                         "the fused cast-and-cast-back, or the per-block / per-channel cast of the "
-                         "workload's input with its code and scale formats")
+                         "the fused cast-and-cast-back, the per-block / per-channel cast of the "
+                         "workload's input with its code and scale formats, RMSNorm forward (bf16 out) "
+                         "or RMSNorm fused with the workload's per-token cast")
     ap.add_argument("--block", default="128x128", help="block rows x block columns for --op per_block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=3, help="distinct input/output sets rotated over")
@@ -205,6 +206,18 @@ def main():
             tk.per_block_cast(xi, br, bc, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si))
         s0 = sets[0][2]
         nbytes = w.rows * (2 * w.cols + w.code_cols) + s0.numel() * s0.element_size()
+    elif args.op == "rmsnorm":
+        wt = (torch.randn(w.cols, generator=torch.Generator().manual_seed(5)) * 0.1 + 1).bfloat16().to(dev)
+
+        def run(xi, qi, si, yi):
+            tk.rmsnorm(xi, wt, 1e-6, "bf16", out=yi)
+        nbytes = w.rows * 4 * w.cols
+    elif args.op == "rmsnorm_cast":
+        wt = (torch.randn(w.cols, generator=torch.Generator().manual_seed(5)) * 0.1 + 1).bfloat16().to(dev)
+
+        def run(xi, qi, si, yi):
+            tk.rmsnorm_cast(xi, wt, 1e-6, w.group, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si))
+        nbytes = w.algorithmic_bytes()
     else:
         ws = torch.empty((tk.tk_per_channel_workspace_bytes(w.rows, w.cols),), dtype=torch.uint8, device=dev)
         sets = [(xi, *tk.per_channel_cast(xi, w.out_dtype, w.round_pow2, w.scale_fmt, workspace=ws))
@@ -214,7 +227,7 @@ def main():
             tk.per_channel_cast(xi, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si), workspace=ws)
         s0 = sets[0][2]
         nbytes = w.rows * (2 * w.cols + w.code_cols) + s0.numel() * s0.element_size()
-    if args.op in ("dequant", "cast_back"):
+    if args.op in ("dequant", "cast_back", "rmsnorm"):
         sets = [(xi, qi, si, torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=dev))
                 for (xi, qi, si) in sets]
     else:
@@ -251,7 +264,7 @@ def main():
         last = sets[(counter[0] - 1) % len(sets)]
         run(*sets[0])
         torch.cuda.synchronize()
-        outs = (3,) if args.op in ("dequant", "cast_back") else (1, 2)
+        outs = (3,) if args.op in ("dequant", "cast_back", "rmsnorm") else (1, 2)
         assert all(torch.equal(last[i].view(torch.uint8), sets[0][i].view(torch.uint8)) for i in outs)
 
     ms_per_step = span_ms / args.steps

@@ -215,6 +215,41 @@ tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t
                               int32_t round_pow2, int32_t scale_fmt, void *stream);
 
 /*
+ * tk_rmsnorm -- RMSNorm forward ("TileKernels" (aiwiki.ai), Version 2.0.0:
+ * RMSNorm forward, with an optional fused FP8 cast).  For each row of C
+ * values, with a per-channel weight w (or none, i.e. all ones) and eps > 0:
+ *     ss  = sum_j x_j^2, the exact sum rounded once to fp32 (nearest-even)
+ *     t   = fl32(fl32(ss / C) + eps)
+ *     r   = fl32(1 / fl32(sqrt(t)))                 (IEEE division and sqrt)
+ *     y_j = fl32(x_j * r), then fl32(y_j * w_j) with a weight
+ * written as fp32 (TK_OUT_F32) or rounded to bf16, nearest-even (TK_OUT_BF16).
+ *
+ *   x        bf16 [rows, cols], row stride x_ld elements.
+ *   cols     a multiple of 8, at most 16384 (larger: TK_ERROR_UNSUPPORTED).
+ *   weight   bf16 [cols] (16-byte aligned), or NULL for no weight.
+ *   eps      finite, > 0.
+ *   y        bf16 or fp32 [rows, cols], row stride y_ld elements.
+ * Alignment: x, y and both row strides in bytes multiples of 16.  Rows whose
+ * sum of squares exceeds the fp32 range give r = 0 (y = +-0).
+ */
+tk_status tk_rmsnorm(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
+                     const void *weight, float eps, void *y, int64_t y_ld, int32_t y_dtype,
+                     void *stream);
+
+/*
+ * tk_rmsnorm_cast -- RMSNorm forward fused with the per-token cast of its
+ * fp32 output y (see tk_rmsnorm): codes and scales exactly as
+ * tk_per_token_cast_f32 would produce from y, without y ever being written.
+ * x, cols, weight, eps as for tk_rmsnorm (cols a multiple of group); q,
+ * q_ld, scales, s_ld, group, out_dtype, round_pow2, scale_fmt, alignment and
+ * errors as for tk_per_token_cast.
+ */
+tk_status tk_rmsnorm_cast(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
+                          const void *weight, float eps, void *q, int64_t q_ld,
+                          void *scales, int64_t s_ld, int32_t group, int32_t out_dtype,
+                          int32_t round_pow2, int32_t scale_fmt, void *stream);
+
+/*
  * tk_silu32_bf16 -- diagnostic: out[i] = silu32(g[i]) for n bf16 gates, by the
  * same device lookup that tk_swiglu_per_token_cast uses for its gate half
  * (fp32 nearest to g / (1 + e^-g)).  g: bf16 [n] (2-byte aligned), out: fp32

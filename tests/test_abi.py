@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     for n in ("tk_per_token_cast", "tk_swiglu_per_token_cast", "tk_status_string", "tk_abi_version",
               "tk_prepare_device", "tk_silu32_bf16", "tk_copy_stream", "tk_per_token_dequant",
               "tk_per_token_cast_back", "tk_per_token_cast_f32", "tk_per_block_cast", "tk_per_channel_cast",
-              "tk_per_channel_workspace_bytes"):
+              "tk_per_channel_workspace_bytes", "tk_rmsnorm", "tk_rmsnorm_cast"):
         assert n in names
 
 
@@ -206,6 +206,36 @@ def test_per_channel_workspace_size():
     assert tk.tk_per_channel_workspace_bytes(65, 256) == 2 * 256 * 2
     assert tk.tk_per_channel_workspace_bytes(4096, 7168) == 32 * 7168 * 2
     assert tk.tk_per_channel_workspace_bytes(10**6, 16) <= 32 * 16 * 2
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(cols=100), INVALID), (dict(cols=0), INVALID), (dict(rows=-1), INVALID), (dict(x_ld=100), INVALID),
+    (dict(y_ld=100), INVALID), (dict(eps=0.0), INVALID), (dict(eps=-1e-6), INVALID), (dict(eps=float("inf")), INVALID),
+    (dict(eps=float("nan")), INVALID), (dict(y_dtype=2), INVALID), (dict(x=0), INVALID), (dict(y=0), INVALID),
+    (dict(x=X + 8), MISALIGNED), (dict(y=Y + 8), MISALIGNED), (dict(w=W + 8), MISALIGNED), (dict(x_ld=260), MISALIGNED),
+    (dict(cols=16392, x_ld=16392, y_ld=16392), UNSUPPORTED), (dict(rows=0, x=0, y=0), 0),
+])
+def test_rmsnorm_validation(kw, want):
+    a = dict(x=X, rows=4, cols=256, x_ld=256, w=W, eps=1e-6, y=Y, y_ld=256, y_dtype=0)
+    a.update(kw)
+    assert tk.tk_rmsnorm(a["x"], a["rows"], a["cols"], a["x_ld"], a["w"], a["eps"], a["y"], a["y_ld"], a["y_dtype"],
+                         0) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(group=48), INVALID), (dict(cols=200), INVALID), (dict(out_dtype=2), INVALID), (dict(scale_fmt=2), INVALID),
+    (dict(scale_fmt=1, round_pow2=0), INVALID), (dict(scale_fmt=1, cols=96), INVALID), (dict(q_ld=100), INVALID),
+    (dict(s_ld=1), INVALID), (dict(eps=0.0), INVALID), (dict(x=0), INVALID), (dict(q=0), INVALID),
+    (dict(s=0), INVALID), (dict(x=X + 8), MISALIGNED), (dict(q=Q + 4), MISALIGNED), (dict(s=S + 2), MISALIGNED),
+    (dict(w=W + 8), MISALIGNED), (dict(cols=16384 + 128, x_ld=16512, q_ld=16512, s_ld=516), UNSUPPORTED),
+    (dict(rows=0, x=0, q=0, s=0), 0),
+])
+def test_rmsnorm_cast_validation(kw, want):
+    a = dict(x=X, rows=4, cols=256, x_ld=256, w=W, eps=1e-6, q=Q, q_ld=256, s=S, s_ld=8, group=32, out_dtype=0,
+             round_pow2=1, scale_fmt=0)
+    a.update(kw)
+    assert tk.tk_rmsnorm_cast(a["x"], a["rows"], a["cols"], a["x_ld"], a["w"], a["eps"], a["q"], a["q_ld"], a["s"],
+                              a["s_ld"], a["group"], a["out_dtype"], a["round_pow2"], a["scale_fmt"], 0) == want
 
 
 def test_copy_stream_validation():
