@@ -26,7 +26,8 @@ sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, AMD published peak
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
-KERNEL_SRC = ROOT / "activation_quantization_token_amd" / "csrc" / "tk_quant.hip"
+# the per-token cast kernels' sources: their hash keys the stored counter runs
+KERNEL_SRCS = [ROOT / "activation_quantization_token_amd" / "csrc" / n for n in ("tk_quant.hip", "tk_device.h")]
 
 
 def log(msg):
@@ -34,7 +35,10 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for src in KERNEL_SRCS:
+        h.update(src.read_bytes())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload_index: int):
