@@ -115,17 +115,25 @@ __device__ __forceinline__ Scale<QD, POW2> group_scale(uint32_t amax_bits)
     constexpr float D = (QD == kE4M3) ? 448.0f : 6.0f;
     const float a = fmaxf(__uint_as_float(amax_bits), 1e-4f);
     Scale<QD, POW2> r;
-    r.s = a / D;                           // IEEE fp32 division
     r.inv = 0.0f;
     r.e8 = 0;
     if constexpr (POW2) {
-        // s is normal (>= 1e-4f / 448): 2^ceil(log2 s) from the exponent and
-        // mantissa fields; E lies in [105, 253], so 2^(127-E) is normal too.
-        const uint32_t b = __float_as_uint(r.s);
-        const uint32_t E = (b >> 23) + ((b & 0x7FFFFFu) != 0u);
+        // 2^ceil(log2 fl32(a / D)) without the division.  D = 7 * 2^6 (E4M3)
+        // or 3 * 2 (E2M1): a / D is a power of two only for a = D * 2^k, and
+        // otherwise lies more than half an fp32 unit from every power of two,
+        // so fl32(a / D) is a power of two exactly when a / D is.  Hence
+        // ceil(log2(a / D)) = e(a) - 8 + (m(a) > 1.75) for E4M3 and
+        // e(a) - 2 + (m(a) > 1.5) for E2M1 (e, m: a's unbiased exponent and
+        // significand).  a >= 1e-4 (exponent field 113) puts E in [105, 253],
+        // so 2^(127-E) is normal too.
+        const uint32_t b = __float_as_uint(a);
+        const uint32_t E = QD == kE4M3 ? (b >> 23) - 8u + ((b & 0x7FFFFFu) > 0x600000u)
+                                       : (b >> 23) - 2u + ((b & 0x7FFFFFu) > 0x400000u);
         r.e8 = E;
         r.s = __uint_as_float(E << 23);
         r.inv = __uint_as_float((254u - E) << 23);
+    } else {
+        r.s = a / D;                       // IEEE fp32 division
     }
     return r;
 }

@@ -57,3 +57,36 @@ def test_table_values_keep_a_margin_from_fp32_midpoints():
             worst = min(worst, float(abs(frac - Fraction(1, 2))))
     assert worst > 2.0 ** -20, worst
 
+
+
+def _pow2_by_division(a: np.ndarray, d: float) -> np.ndarray:
+    """Biased exponent of 2^ceil(log2(fl32(a / d))) read from the quotient's fields."""
+    s = (a / np.float32(d)).astype(np.float32).view(np.uint32)
+    return (s >> 23) + ((s & 0x7FFFFF) != 0)
+
+
+def _pow2_by_fields(a: np.ndarray, qd: str) -> np.ndarray:
+    """The kernels' division-free form: from a's own exponent and mantissa."""
+    b = a.view(np.uint32)
+    e, m = b >> 23, b & 0x7FFFFF
+    if qd == "e4m3":                       # D = 7 * 2^6: round up past mantissa 1.75
+        return e - 8 + (m > 0x600000)
+    return e - 2 + (m > 0x400000)          # D = 3 * 2: round up past mantissa 1.5
+
+
+def test_pow2_scale_without_division():
+    """fl32(a/448) and fl32(a/6) are powers of two only when the exact
+    quotients are, so ceil(log2) of the rounded quotient follows from a's
+    fields: checked for every fp32 significand at exponents spanning the
+    floored range [1e-4, FLT_MAX], and at the floor itself."""
+    mant = np.arange(1 << 23, dtype=np.uint32)
+    floor_bits = np.float32(1e-4).view(np.uint32)
+    for field in (113, 114, 120, 127, 128, 150, 200, 253, 254):
+        bits = (np.uint32(field) << 23) | mant
+        if field == 113:
+            bits = bits[bits >= floor_bits]
+        a = bits.view(np.float32)
+        for qd, d in (("e4m3", 448.0), ("e2m1", 6.0)):
+            want = _pow2_by_division(a, d)
+            got = _pow2_by_fields(a, qd)
+            assert np.array_equal(got, want), (field, qd, int(np.argmax(got != want)))
