@@ -255,6 +255,17 @@ def test_binding_rejects_cpu_tensors():
         tk.per_token_cast(x.float(), 32)
 
 
+def test_header_is_plain_c_and_links():
+    """include/tk_quant.h compiles as C11 and every call the C driver makes
+    links against the built library (the driver runs in the GPU tests)."""
+    import importlib.util
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "build_check.py")
+    spec = importlib.util.spec_from_file_location("c_abi_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert mod.build().exists()
+
+
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         binding.load_library(tmp_path / "libtk_quant.so")
