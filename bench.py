@@ -102,33 +102,74 @@ def summarize_pmc(workload_index, fetch_csv, write_csv):
     print(json.dumps(entry, indent=2))
 
 
-def cpu_baseline(w, x_bits, threads: int, min_wall_s: float = 1.0, max_passes: int = 20):
-    """The CPU oracle over row blocks on `threads` host threads: whole passes
-    over the workload (at most its first 32768 rows) until `min_wall_s` of wall
-    time has elapsed, i.e. about threads * min_wall_s seconds of CPU work."""
+def _oracle_step(op: str, w, block, weight_bits):
+    """(fn(rows of x) -> None, rows must be a multiple of, algorithmic bytes per row)
+    for one operation's CPU oracle; the per-row byte count matches the bench's."""
     import numpy as np
     import oracle
-    fn = oracle.swiglu_per_token_cast if w.swiglu else oracle.per_token_cast
+    code_cols = w.code_cols
+    if op == "cast":
+        fn = oracle.swiglu_per_token_cast if w.swiglu else oracle.per_token_cast
+        return (lambda xs: fn(xs, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)), 1, w.algorithmic_bytes(1)
+    if op == "dequant":
+        def run(xs):
+            q, s = oracle.per_token_cast(xs, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)
+            oracle.per_token_dequant(q, s, w.cols, w.group, w.out_dtype, w.scale_fmt, "bf16")
+        # the cast that makes the codes runs inside the timed oracle step too: its bytes are counted
+        return run, 1, w.algorithmic_bytes(1) + code_cols + 4 * w.scale_cols + 2 * w.cols
+    if op == "cast_back":
+        return (lambda xs: oracle.per_token_cast_back(xs, w.group, w.out_dtype, w.round_pow2)), 1, 4 * w.cols
+    if op == "per_block":
+        br, bc = block
+        nbc = w.cols // bc
+        sbytes = 4 * nbc if w.scale_fmt == "f32" else nbc
+        return ((lambda xs: oracle.per_block_cast(xs, br, bc, w.out_dtype, w.round_pow2, w.scale_fmt)), br,
+                2 * w.cols + code_cols + sbytes / br)
+    if op == "per_channel":
+        return ((lambda xs: oracle.per_channel_cast(xs, w.out_dtype, w.round_pow2, w.scale_fmt)), 1,
+                2 * w.cols + code_cols)
+    if op == "rmsnorm_cast":
+        return ((lambda xs: oracle.rmsnorm_cast(xs, weight_bits, 1e-6, w.group, w.out_dtype, w.round_pow2,
+                                                w.scale_fmt)), 1, w.algorithmic_bytes(1))
+    if op == "rmsnorm":
+        return (lambda xs: oracle.rmsnorm(xs, weight_bits, 1e-6, "bf16")), 1, 4 * w.cols
+    raise ValueError(op)
+
+
+def cpu_baseline(w, x_bits, threads: int, op: str = "cast", block=(128, 128), weight_bits=None,
+                 min_wall_s: float = 1.0, max_passes: int = 20):
+    """The operation's CPU oracle over row blocks on `threads` host threads:
+    whole passes over the workload's first rows (at most 32768, rounded to the
+    block height) until `min_wall_s` of wall time has elapsed, i.e. about
+    threads * min_wall_s seconds of CPU work.  The per-channel oracle, whose
+    column maxima span all rows, runs over column blocks instead."""
+    import numpy as np
+    fn, unit, bytes_per_row = _oracle_step(op, w, block, weight_bits)
     rows = x_bits.shape[0]
-    sample = min(rows, 32768)
+    sample = min(rows, 32768) // unit * unit
     xs = x_bits[:sample]
-    bounds = np.linspace(0, sample, threads + 1).astype(int)
-    fn(xs[:8], w.group, w.out_dtype, w.round_pow2, w.scale_fmt)          # load the library
+    if op == "per_channel":
+        cuts = np.linspace(0, w.cols // 8, threads + 1).astype(int) * 8
+        parts = [np.ascontiguousarray(xs[:, cuts[i]:cuts[i + 1]]) for i in range(threads)]
+    else:
+        cuts = (np.linspace(0, sample // unit, threads + 1).astype(int) * unit)
+        parts = [xs[cuts[i]:cuts[i + 1]] for i in range(threads)]
+    fn(parts[0][:unit] if op != "per_channel" else parts[0][:8])          # load the library
     passes = 0
     t0 = time.perf_counter()
     with concurrent.futures.ThreadPoolExecutor(threads) as ex:
         while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_wall_s):
-            list(ex.map(lambda i: fn(xs[bounds[i]:bounds[i + 1]], w.group, w.out_dtype, w.round_pow2,
-                                     w.scale_fmt), range(threads)))
+            list(ex.map(fn, parts))
             passes += 1
     dt = time.perf_counter() - t0
+    nbytes = bytes_per_row * sample
     return {
-        "value": round(passes * w.algorithmic_bytes(sample) / dt / 1e9, 3),
+        "value": round(passes * nbytes / dt / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"{passes} passes over rows 0..{sample - 1} of the workload ({sample} x {w.in_cols} bf16), "
-                  f"{threads} threads over row blocks, {dt:.2f} s wall",
+                  f"{threads} threads over {'column' if op == 'per_channel' else 'row'} blocks, {dt:.2f} s wall",
         "tokens_per_s": round(passes * sample / dt, 1),
     }
 
@@ -320,10 +361,14 @@ def main():
         for _ in range(3):
             tk.copy_stream(src, dst)
         torch.cuda.synchronize()
-    if not args.no_cpu_baseline and args.op == "cast":
+    if not args.no_cpu_baseline:
         threads = min(16, len(os.sched_getaffinity(0)))
         log(f"[bench] CPU baseline: oracle on {threads} threads")
-        out["cpu_baseline"] = cpu_baseline(w, x_bits, threads)
+        weight_bits = None
+        if args.op in ("rmsnorm", "rmsnorm_cast"):
+            weight_bits = wt.cpu().view(torch.int16).numpy().view(np.uint16)
+        block = tuple(int(v) for v in args.block.split("x"))
+        out["cpu_baseline"] = cpu_baseline(w, x_bits, threads, args.op, block, weight_bits)
     print(json.dumps(out), flush=True)
 
 
