@@ -4,25 +4,26 @@
 // contract is written out in include/tk_quant.h.
 //
 // Design.  The fused cast of rows of up to 7168 channels runs one row per
-// wave (see rmsnorm_wave_kernel below).  Otherwise a workgroup owns one row
-// at a time (a persistent grid strides over the rows, each workgroup prefetching
-// its next row) and holds the whole row in registers: W = ceil(cols / 1024) waves, each lane 2
-// segments of 8 bf16 (16-byte loads, 1 KiB per wave instruction), so rows of
-// up to 16384 channels are read from memory exactly once.  The weight row is
-// loaded once per workgroup into the same lane layout.
+// wave (rmsnorm_wave_kernel below).  Otherwise a workgroup owns one row at a
+// time (a persistent grid strides over the rows, each workgroup prefetching
+// its next row) and holds the whole row in registers: W = ceil(cols / 1024)
+// waves, each lane 2 segments of 8 bf16 (16-byte loads, 1 KiB per wave
+// instruction), so rows of up to 16384 channels are read from memory exactly
+// once.  The weight row is loaded once per workgroup.
 //
 // The sum of squares is defined as the exact sum rounded once to fp32.  Each
-// lane sums its squares in fp64 (a bf16 square is exact in fp64), the waves
-// reduce with cross-lane shuffles and through LDS in a fixed order, and the
-// fp64 result D is certified: the exact sum differs from D by at most 37
-// roundings of 2^-53 relative (16 per lane, 6 shuffle levels, up to 15 wave
-// sums), well inside D * 2^-46, so when D +- D * 2^-46 lies strictly between
-// the two fp32 rounding midpoints around fl32(D), fl32(D) is the answer.
-// Otherwise (about one row in 2^20 for random data; also every row whose
-// exact sum sits on a midpoint, and sums outside the fp32 normal range) the
-// workgroup recomputes the sum exactly with an integer accumulator in LDS and
-// rounds it by hand.  Wave 0 alone turns the wave sums into r and hands it to
-// the other waves through LDS.
+// lane sums its squares in fp64 (a bf16 square is exact in fp64), the lanes
+// and waves reduce in a fixed order, and the fp64 result D is certified: the
+// exact sum S differs from D by at most n roundings of 2^-53 relative, n = the
+// additions on any path (workgroup kernel: 16 per lane, 6 shuffle levels, up
+// to 15 wave sums; wave kernel: up to 112 per lane and 6 levels), which is at
+// most n units in the last place of D's binade.  fl32(D) is accepted unless
+// the 29 low mantissa bits that fl32 drops lie within 256 units of the
+// halfway pattern (certified()).  Otherwise (about one row in 2^20 for random
+// data; also every row whose exact sum sits on a midpoint, and sums outside
+// the fp32 normal range) the row is summed again exactly with an integer
+// accumulator in LDS and rounded by hand.  In the workgroup kernel wave 0
+// alone turns the wave sums into r and hands it to the other waves.
 
 #include <hip/hip_runtime.h>
 
@@ -61,12 +62,12 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int mask, int lane)
 }
 
 // True when fl32(D) is certainly the exact sum S rounded to fp32, given
-// |S - D| <= D * 2^-46 (S, D >= 0).  That bound is at most 128 units in the
-// last place of D's fp64 binade, and the fp32 rounding midpoints in that
-// binade are exactly the values whose 29 low mantissa bits (the ones fl32
-// drops) read 2^28.  So fl32(D) is safe unless those bits lie within 256 of
-// 2^28; D outside the fp32 normal range (below 2^-126, or from 2^127 up,
-// where fl32 may overflow) is left to the exact path too.
+// |S - D| below 256 units in the last place of D's binade (S, D >= 0).  The
+// fp32 rounding midpoints in that binade are exactly the values whose 29 low
+// mantissa bits (the ones fl32 drops) read 2^28, so fl32(D) is safe unless
+// those bits lie within 256 of 2^28; D outside the fp32 normal range (below
+// 2^-126, or from 2^127 up, where fl32 may overflow) is left to the exact
+// path too.
 __device__ __forceinline__ bool certified(double d)
 {
     if (d == 0.0) return true;                    // all squares zero: exact
@@ -168,15 +169,8 @@ __device__ __forceinline__ double wave_sum_f64(double v, int lane)
 // Persistent form: a workgroup takes rows blockIdx.x, blockIdx.x + gridDim.x,
 // ... and loads its next row before it reduces the current one, so a row's
 // load latency overlaps the previous row's reduction, barrier and stores.
-#ifndef TK_NORM_WAVES_PER_EU
-#define TK_NORM_WAVES_PER_EU 1
-#endif
-#ifndef TK_NORM_PACKED_WEIGHT
-#define TK_NORM_PACKED_WEIGHT 0
-#endif
 template <int G, int QD, bool POW2, int SF, int OUT>
-__global__ __launch_bounds__(kWave * kNormMaxWaves) __attribute__((amdgpu_waves_per_eu(TK_NORM_WAVES_PER_EU)))
-void rmsnorm_kernel(NormParams p)
+__global__ __launch_bounds__(kWave * kNormMaxWaves) void rmsnorm_kernel(NormParams p)
 {
     extern __shared__ uint32_t row_scales[];      // the row's scale words (cast form)
     __shared__ double wave_sum[kNormMaxWaves];
@@ -213,12 +207,6 @@ void rmsnorm_kernel(NormParams p)
     u32x4 w[kNormU];
     if (row < p.rows) load_row(row, w);
     for (; row < p.rows; row += gridDim.x) {
-#if TK_NORM_PACKED_WEIGHT
-        // keep the weight packed (8 registers) instead of letting the
-        // compiler hoist its widened form (16) out of the loop
-#pragma unroll
-        for (int k = 0; k < kNormU; ++k) asm volatile("" : "+v"(wt[k]));
-#endif
         u32x4 wn[kNormU];
         const int64_t next = row + gridDim.x;
 #pragma unroll

@@ -20,7 +20,11 @@
 // contiguous bytes per wave instruction.  Rows are addressed through buffer
 // resource descriptors whose size is the row's length, so loads past the row
 // end return zero and stores past it are dropped by the hardware: ragged
-// tails need no predication.  All global traffic is non-temporal.
+// tails need no predication.  Inputs and codes stream non-temporally; the
+// short scale rows use write-back stores so that L2 merges their pieces.
+// The plain cast runs the row form (cast_rows_kernel: one workgroup per row,
+// the row's scale words gathered in LDS and stored once); the unit form
+// (cast_kernel) serves rows whose scale words exceed the LDS staging size.
 
 #include <hip/hip_runtime.h>
 
