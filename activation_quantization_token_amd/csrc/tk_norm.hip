@@ -408,19 +408,28 @@ __global__ __launch_bounds__(kWave * kNormWaveWPB) void rmsnorm_wave_kernel(Norm
         lds_weight[t] = t < cols ? (p.w ? __uint_as_float(uint32_t(p.w[t]) << 16) : 1.0f) : 0.0f;
     __syncthreads();                              // the only workgroup barrier
 
+    // Rows wave_id, wave_id + nwaves, ...  Segment k of a lane is byte
+    // lane * 16 + k * 1024 of the row, the segment offset in the instruction's
+    // scalar offset.  The next row's segment k is loaded into xs[k] as soon
+    // as the cast has consumed the current row's, so the next row streams in
+    // while this one is converted.
     const int64_t nwaves = int64_t(gridDim.x) * kNormWaveWPB;
-    for (int64_t row_it = int64_t(blockIdx.x) * kNormWaveWPB + wave; row_it < p.rows; row_it += nwaves) {
-        // the row is the same on every lane; saying so keeps the row
-        // descriptors in scalar registers
-        const int64_t row = int64_t(uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(row_it >> 32)))) << 32 |
-                                    uint32_t(__builtin_amdgcn_readfirstlane(int(row_it))));
-        // segment k of this lane: byte lane * 16 + k * 1024 of the row, the
-        // segment offset in the instruction's scalar offset
+    auto uniform = [](int64_t v) {   // the same on every lane: keeps descriptors in scalar registers
+        return int64_t(uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(v >> 32)))) << 32 |
+                       uint32_t(__builtin_amdgcn_readfirstlane(int(v))));
+    };
+    u32x4 xs[NS];
+    int64_t row = uniform(int64_t(blockIdx.x) * kNormWaveWPB + wave);
+    if (row < p.rows) {
         const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + row * p.x_ld, cols * 2u);
-        u32x4 xs[NS];
 #pragma unroll
         for (int k = 0; k < NS; ++k)
             xs[k] = __builtin_amdgcn_raw_buffer_load_b128(xrow, int(lane * 16), k * kSegCols * 2, kNonTemporal);
+    }
+    for (; row < p.rows; row = uniform(row + nwaves)) {
+        const int64_t next = row + nwaves;
+        const bool has_next = next < p.rows;
+        const __amdgpu_buffer_rsrc_t nrow = row_buffer(p.x + (has_next ? next : row) * p.x_ld, cols * 2u);
         double acc = 0.0;
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
@@ -455,6 +464,8 @@ __global__ __launch_bounds__(kWave * kNormWaveWPB) void rmsnorm_wave_kernel(Norm
                     amax = max(amax, __float_as_uint(y[i]) & 0x7FFFFFFFu);
                 }
                 const Quantized qz = quantize_segment<G, QD, POW2>(y, amax);
+                if (has_next)           // the next row's segment k takes this one's registers
+                    xs[k] = __builtin_amdgcn_raw_buffer_load_b128(nrow, int(lane * 16), k * kSegCols * 2, kNonTemporal);
                 if constexpr (QD == kE4M3)
                     __builtin_amdgcn_raw_buffer_store_b64(qz.codes, qrow, int(lane * 8), k * kSegCols, kNonTemporal);
                 else
