@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     rmsnorm,
     rmsnorm_cast,
     silu32_bf16,
+    stream_rw,
     swiglu_per_token_cast,
     tk_abi_version,
     tk_copy_stream,
@@ -35,6 +36,7 @@ from .binding import (  # noqa: F401
     tk_rmsnorm,
     tk_rmsnorm_cast,
     tk_silu32_bf16,
+    tk_stream_rw,
     tk_status_string,
     tk_swiglu_per_token_cast,
 )

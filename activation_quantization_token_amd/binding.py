@@ -72,6 +72,8 @@ def load_library(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
         lib.tk_silu32_bf16.restype = ctypes.c_int
         lib.tk_copy_stream.argtypes = [vp, vp, i64, vp]
         lib.tk_copy_stream.restype = ctypes.c_int
+        lib.tk_stream_rw.argtypes = [vp, i64, vp, i64, vp]
+        lib.tk_stream_rw.restype = ctypes.c_int
         lib.tk_prepare_device.argtypes = []
         lib.tk_prepare_device.restype = ctypes.c_int
         lib.tk_status_string.argtypes = [i32]
@@ -136,6 +138,20 @@ def copy_stream(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     if dst.numel() * dst.element_size() < n:
         raise ValueError("dst is smaller than src")
     _check(tk_copy_stream(src.data_ptr(), dst.data_ptr(), n, _stream_handle(stream, src.device)))
+
+
+def tk_stream_rw(src: int, read_bytes: int, dst: int, write_bytes: int, stream: int) -> int:
+    """Raw C call: streaming-ceiling diagnostic; returns the tk_status code."""
+    return load_library().tk_stream_rw(src, read_bytes, dst, write_bytes, stream)
+
+
+def stream_rw(src: torch.Tensor, read_bytes: int, dst: torch.Tensor, write_bytes: int, stream=None) -> None:
+    """Diagnostic: read `read_bytes` of src and write `write_bytes` of dst (the
+    cast's memory instructions; practical streaming ceiling)."""
+    for t, n in ((src, read_bytes), (dst, write_bytes)):
+        if not t.is_cuda or not t.is_contiguous() or t.numel() * t.element_size() < n:
+            raise ValueError("src and dst must be contiguous GPU tensors holding the byte counts")
+    _check(tk_stream_rw(src.data_ptr(), read_bytes, dst.data_ptr(), write_bytes, _stream_handle(stream, src.device)))
 
 
 def tk_per_token_cast(x: int, rows: int, cols: int, x_ld: int, q: int, q_ld: int, scales: int,

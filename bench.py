@@ -163,6 +163,19 @@ def cpu_baseline(w, x_bits, threads: int, op: str = "cast", block=(128, 128), we
             passes += 1
     dt = time.perf_counter() - t0
     nbytes = bytes_per_row * sample
+    # one core: the first 1/threads of the sample, whole passes for >= 1 s
+    one, t1, p1 = parts[0], time.perf_counter(), 0
+    while p1 < max_passes and (p1 == 0 or time.perf_counter() - t1 < min_wall_s):
+        fn(one)
+        p1 += 1
+    d1 = time.perf_counter() - t1
+    one_bytes = bytes_per_row * (one.shape[0] if op != "per_channel" else sample) * \
+        (1 if op != "per_channel" else one.shape[1] / w.cols)
+    model = ""
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {
         "value": round(passes * nbytes / dt / 1e9, 3),
         "unit": "GB/s",
@@ -171,6 +184,9 @@ def cpu_baseline(w, x_bits, threads: int, op: str = "cast", block=(128, 128), we
         "sample": f"{passes} passes over rows 0..{sample - 1} of the workload ({sample} x {w.in_cols} bf16), "
                   f"{threads} threads over {'column' if op == 'per_channel' else 'row'} blocks, {dt:.2f} s wall",
         "tokens_per_s": round(passes * sample / dt, 1),
+        "single_core": {"value": round(p1 * one_bytes / d1 / 1e9, 4), "unit": "GB/s",
+                        "sample": f"{p1} passes over one thread's share, {d1:.2f} s"},
+        "cpu_model": model,
     }
 
 
@@ -189,6 +205,8 @@ def main():
     ap.add_argument("--block", default="128x128", help="block rows x block columns for --op per_block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=3, help="distinct input/output sets rotated over")
+    ap.add_argument("--flushed", type=int, default=50,
+                    help="extra launches timed one by one, each after a 512 MiB copy that flushes the caches")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run 3 device-to-device copies of 1 GiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -230,6 +248,7 @@ def main():
         def run(xi, qi, si, yi):
             fn(xi, w.group, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si))
         nbytes = w.algorithmic_bytes()
+        read_bytes = w.rows * w.in_cols * 2
     elif args.op == "dequant":
         # inputs: the workload's codes and scales (made by the cast); output bf16
         for i in range(len(sets)):
@@ -239,10 +258,12 @@ def main():
         def run(xi, qi, si, yi):
             tk.per_token_dequant(qi, si, w.cols, w.group, w.out_dtype, w.scale_fmt, "bf16", out=yi)
         nbytes = w.rows * (w.code_cols + 4 * w.scale_cols + 2 * w.cols)
+        read_bytes = w.rows * (w.code_cols + 4 * w.scale_cols)
     elif args.op == "cast_back":
         def run(xi, qi, si, yi):
             tk.per_token_cast_back(xi, w.group, w.out_dtype, w.round_pow2, out=yi)
         nbytes = w.rows * 4 * w.cols
+        read_bytes = w.rows * 2 * w.cols
     elif args.op == "per_block":
         br, bc = (int(v) for v in args.block.split("x"))
         sets = [(xi, *tk.per_block_cast(xi, br, bc, w.out_dtype, w.round_pow2, w.scale_fmt)) for (xi, _, _) in sets]
@@ -251,18 +272,21 @@ def main():
             tk.per_block_cast(xi, br, bc, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si))
         s0 = sets[0][2]
         nbytes = w.rows * (2 * w.cols + w.code_cols) + s0.numel() * s0.element_size()
+        read_bytes = w.rows * 2 * w.cols
     elif args.op == "rmsnorm":
         wt = (torch.randn(w.cols, generator=torch.Generator().manual_seed(5)) * 0.1 + 1).bfloat16().to(dev)
 
         def run(xi, qi, si, yi):
             tk.rmsnorm(xi, wt, 1e-6, "bf16", out=yi)
         nbytes = w.rows * 4 * w.cols
+        read_bytes = w.rows * 2 * w.cols
     elif args.op == "rmsnorm_cast":
         wt = (torch.randn(w.cols, generator=torch.Generator().manual_seed(5)) * 0.1 + 1).bfloat16().to(dev)
 
         def run(xi, qi, si, yi):
             tk.rmsnorm_cast(xi, wt, 1e-6, w.group, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si))
         nbytes = w.algorithmic_bytes()
+        read_bytes = w.rows * 2 * w.cols
     else:
         ws = torch.empty((tk.tk_per_channel_workspace_bytes(w.rows, w.cols),), dtype=torch.uint8, device=dev)
         sets = [(xi, *tk.per_channel_cast(xi, w.out_dtype, w.round_pow2, w.scale_fmt, workspace=ws))
@@ -272,6 +296,7 @@ def main():
             tk.per_channel_cast(xi, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si), workspace=ws)
         s0 = sets[0][2]
         nbytes = w.rows * (2 * w.cols + w.code_cols) + s0.numel() * s0.element_size()
+        read_bytes = w.rows * 2 * w.cols
     if args.op in ("dequant", "cast_back", "rmsnorm"):
         sets = [(xi, qi, si, torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=dev))
                 for (xi, qi, si) in sets]
@@ -311,6 +336,44 @@ def main():
         torch.cuda.synchronize()
         outs = (3,) if args.op in ("dequant", "cast_back", "rmsnorm") else (1, 2)
         assert all(torch.equal(last[i].view(torch.uint8), sets[0][i].view(torch.uint8)) for i in outs)
+
+    # Per-launch durations with the 256 MB Infinity Cache flushed before each
+    # launch (a 512 MiB streaming copy in between), event-timed one by one.
+    flush_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+    per_launch = []
+    for i in range(args.flushed):
+        tk.copy_stream(flush_src, flush_dst)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run(*sets[i % len(sets)])
+        b.record(stream)
+        b.synchronize()
+        per_launch.append(a.elapsed_time(b) * 1e3)
+    del flush_src, flush_dst
+    flushed = None
+    if per_launch:
+        pl = np.sort(np.array(per_launch))
+        med = float(np.median(pl))
+        flushed = {"launches": len(pl), "median_us": round(med, 3), "p10_us": round(float(np.percentile(pl, 10)), 3),
+                   "p90_us": round(float(np.percentile(pl, 90)), 3), "median_gbs": round(nbytes / med / 1e3, 2)}
+
+    # Practical streaming ceiling for the same read and write volumes: the
+    # library's stream diagnostic, timed exactly like the operation.
+    rd, wr = read_bytes - read_bytes % 16, (nbytes - read_bytes) - (nbytes - read_bytes) % 16
+    csrc = [torch.empty(rd, dtype=torch.uint8, device=dev) for _ in range(len(sets))]
+    cdst = [torch.empty(wr, dtype=torch.uint8, device=dev) for _ in range(len(sets))]
+    for i in range(args.warmup):
+        tk.stream_rw(csrc[i % len(sets)], rd, cdst[i % len(sets)], wr)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for i in range(args.steps):
+        tk.stream_rw(csrc[i % len(sets)], rd, cdst[i % len(sets)], wr)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    ceil_us = c0.elapsed_time(c1) * 1e3 / args.steps
+    del csrc, cdst
 
     ms_per_step = span_ms / args.steps
     value = nbytes * args.steps / (span_ms / 1e3) / 1e9
@@ -354,6 +417,13 @@ def main():
             "algorithmic_bytes_per_launch": nbytes,
             "buffer_sets": len(sets),
         },
+        "ceiling": {
+            "kernel": "tk_stream_rw (the same read and write bytes, the cast's memory instructions)",
+            "read_bytes": rd, "write_bytes": wr, "us": round(ceil_us, 3),
+            "gbs": round(nbytes / ceil_us / 1e3, 2), "frac_of_peak": round(nbytes / ceil_us / 1e3 / HBM_PEAK_GBS, 4),
+            "op_frac_of_ceiling": round(ceil_us / ms_per_step / 1e3, 4),
+        },
+        "flushed": flushed,
     }
     if args.calibrate_copy:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)

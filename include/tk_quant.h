@@ -269,6 +269,19 @@ tk_status tk_silu32_bf16(const void *g, void *out, int64_t n, void *stream);
 tk_status tk_copy_stream(const void *src, void *dst, int64_t bytes, void *stream);
 
 /*
+ * tk_stream_rw -- diagnostic: read `read_bytes` from src and write
+ * `write_bytes` to dst with the cast's memory instructions (16-byte
+ * non-temporal loads and stores), each workgroup reading a contiguous 64 KiB
+ * of the larger stream and the proportional contiguous piece of the other.  The written values are a running xor of what was read (every
+ * load is kept); their contents are otherwise meaningless.  Used as the
+ * practical streaming ceiling of an operation with the same read and write
+ * volumes.  Sizes multiples of 16, both nonzero (or both zero: nothing to
+ * do), pointers 16-byte aligned (TK_ERROR_INVALID_VALUE /
+ * TK_ERROR_MISALIGNED otherwise); sizes below 2^35 (TK_ERROR_UNSUPPORTED).
+ */
+tk_status tk_stream_rw(const void *src, int64_t read_bytes, void *dst, int64_t write_bytes, void *stream);
+
+/*
  * tk_prepare_device -- build the per-device tables used by the SwiGLU form on
  * the current HIP device, and wait until they are ready.  Idempotent; safe to
  * call from several threads.

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     for n in ("tk_per_token_cast", "tk_swiglu_per_token_cast", "tk_status_string", "tk_abi_version",
               "tk_prepare_device", "tk_silu32_bf16", "tk_copy_stream", "tk_per_token_dequant",
               "tk_per_token_cast_back", "tk_per_token_cast_f32", "tk_per_block_cast", "tk_per_channel_cast",
-              "tk_per_channel_workspace_bytes", "tk_rmsnorm", "tk_rmsnorm_cast"):
+              "tk_per_channel_workspace_bytes", "tk_rmsnorm", "tk_rmsnorm_cast", "tk_stream_rw"):
         assert n in names
 
 
@@ -244,6 +244,16 @@ def test_copy_stream_validation():
     assert tk.tk_copy_stream(X, Q, 0, 0) == 0
     assert tk.tk_copy_stream(0, Q, 32, 0) == INVALID
     assert tk.tk_copy_stream(X + 8, Q, 32, 0) == MISALIGNED
+
+
+def test_stream_rw_validation():
+    assert tk.tk_stream_rw(X, -16, Q, 0, 0) == INVALID
+    assert tk.tk_stream_rw(X, 24, Q, 0, 0) == INVALID
+    assert tk.tk_stream_rw(X, 32, Q, 0, 0) == INVALID           # one stream empty
+    assert tk.tk_stream_rw(X, 0, Q, 0, 0) == 0
+    assert tk.tk_stream_rw(0, 32, Q, 16, 0) == INVALID
+    assert tk.tk_stream_rw(X + 8, 32, Q, 16, 0) == MISALIGNED
+    assert tk.tk_stream_rw(X, 1 << 35, Q, 16, 0) == UNSUPPORTED
 
 
 def test_binding_rejects_cpu_tensors():

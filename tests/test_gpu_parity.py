@@ -248,6 +248,23 @@ def test_copy_stream_copies():
     assert torch.equal(src, dst)
 
 
+@pytest.mark.parametrize("read_mib,write_mib", [(4, 1), (3, 3), (1, 5)])
+def test_stream_rw_writes_every_unit(read_mib, write_mib):
+    """The streaming-ceiling diagnostic reads its source and writes every
+    16-byte unit of its destination (canaries past the end stay)."""
+    log(f"[gpu] stream_rw {read_mib} MiB -> {write_mib} MiB")
+    src = torch.randint(1, 2**31 - 1, (read_mib << 18,), dtype=torch.int32, device="cuda")
+    n = write_mib << 18
+    sentinel = -0x5A5A5A5B                      # 0xA5A5A5A5
+    dst = torch.full((n + 64,), sentinel, dtype=torch.int32, device="cuda")
+    tk.stream_rw(src, read_mib << 20, dst, write_mib << 20)
+    torch.cuda.synchronize()
+    units = dst[:n].view(-1, 4).cpu().numpy()
+    untouched = np.all(units == sentinel, axis=1)
+    assert np.count_nonzero(untouched) <= 1, "units left unwritten"   # equal to the sentinel only by chance
+    assert bool((dst[n:] == sentinel).all().item()), "write past the end"
+
+
 def test_side_stream_and_reuse():
     log("[gpu] side stream")
     x_bits = inputs.generate_small(1, 64, 7168)
