@@ -199,6 +199,17 @@ def empty_outputs(rows: int, cols: int, group: int, out_dtype: str, scale_fmt: s
     return q, s
 
 
+def _check_out_shapes(q, s, q_cols, s_cols, scale_fmt):
+    """Caller-given outputs: dtypes, and room for every column the call writes."""
+    if q.dtype != torch.uint8:
+        raise TypeError("codes must be uint8")
+    want = torch.float32 if scale_fmt == "f32" else torch.int32
+    if s.dtype != want:
+        raise TypeError(f"scales must be {want} for scale_fmt {scale_fmt!r}")
+    if q.shape[-1] < q_cols or s.shape[-1] < s_cols:
+        raise ValueError(f"outputs too narrow: codes need {q_cols} columns, scales {s_cols}")
+
+
 def _run(fn, x, cols, group, out_dtype, round_pow2, scale_fmt, out, stream):
     if group not in GROUPS:
         raise ValueError(f"group must be one of {GROUPS}")
@@ -214,6 +225,8 @@ def _run(fn, x, cols, group, out_dtype, round_pow2, scale_fmt, out, stream):
     for t in (q, s):
         if t.device != x.device or t.dim() != 2 or t.stride(1) != 1 or t.shape[0] != rows:
             raise ValueError("outputs must be 2-D, row-contiguous, on the input's device")
+    _check_out_shapes(q, s, cols if out_dtype == "e4m3" else cols // 2,
+                      cols // group if scale_fmt == "f32" else cols // group // 4, scale_fmt)
     st = fn(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0), s.data_ptr(),
             s.stride(0), group, QDTYPES[out_dtype], int(bool(round_pow2)), SCALE_FMTS[scale_fmt],
             _stream_handle(stream, x.device))
@@ -267,13 +280,21 @@ def per_token_dequant(q: torch.Tensor, scales: torch.Tensor, cols: int, group: i
     for t, what in ((q, "q"), (scales, "scales")):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
             raise TypeError(f"{what} must be a 2-D row-contiguous GPU tensor")
-    if q.dtype != torch.uint8:
-        raise TypeError("q must be uint8")
+    _check_formats(in_dtype, scale_fmt)
+    if out_dtype not in OUT_DTYPES:
+        raise ValueError("out_dtype must be 'bf16'|'f32'")
+    if group not in GROUPS or cols <= 0 or cols % group or (scale_fmt == "ue8m0" and (cols // group) % 4):
+        raise ValueError("cols must be a positive multiple of group (of 4*group for ue8m0 scales)")
     rows = q.shape[0]
+    if scales.shape[0] != rows or scales.device != q.device:
+        raise ValueError("scales must have q's rows, on q's device")
+    _check_out_shapes(q, scales, cols if in_dtype == "e4m3" else cols // 2,
+                      cols // group if scale_fmt == "f32" else cols // group // 4, scale_fmt)
     ydt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
     y = torch.empty((rows, cols), dtype=ydt, device=q.device) if out is None else out
-    if y.dtype != ydt or y.dim() != 2 or y.stride(1) != 1 or y.shape[0] != rows or y.device != q.device:
-        raise ValueError("out must be a row-contiguous tensor of the output dtype on q's device")
+    if (y.dtype != ydt or y.dim() != 2 or y.stride(1) != 1 or tuple(y.shape) != (rows, cols)
+            or y.device != q.device):
+        raise ValueError("out must be a row-contiguous [rows, cols] tensor of the output dtype on q's device")
     _check(tk_per_token_dequant(q.data_ptr(), rows, cols, q.stride(0), scales.data_ptr(), scales.stride(0),
                                 group, QDTYPES[in_dtype], SCALE_FMTS[scale_fmt], y.data_ptr(), y.stride(0),
                                 OUT_DTYPES[out_dtype], _stream_handle(stream, q.device)))
@@ -286,8 +307,11 @@ def per_token_cast_back(x: torch.Tensor, group: int = 128, out_dtype: str = "e4m
     _check_input(x, "x")
     rows, cols = x.shape
     y = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device) if out is None else out
-    if y.dtype != torch.bfloat16 or y.dim() != 2 or y.stride(1) != 1 or tuple(y.shape) != (rows, cols):
-        raise ValueError("out must be a row-contiguous bf16 tensor of x's shape")
+    if (y.dtype != torch.bfloat16 or y.dim() != 2 or y.stride(1) != 1 or tuple(y.shape) != (rows, cols)
+            or y.device != x.device):
+        raise ValueError("out must be a row-contiguous bf16 tensor of x's shape on x's device")
+    if out_dtype not in QDTYPES:
+        raise ValueError("out_dtype must be 'e4m3'|'e2m1'")
     _check(tk_per_token_cast_back(x.data_ptr(), rows, cols, x.stride(0), y.data_ptr(), y.stride(0), group,
                                   QDTYPES[out_dtype], int(bool(round_pow2)), _stream_handle(stream, x.device)))
     return y
@@ -341,6 +365,8 @@ def per_block_cast(x: torch.Tensor, block_rows: int = 128, block_cols: int = 128
             raise ValueError("outputs must be 2-D, row-contiguous, on the input's device")
     if q.shape[0] != rows or s.shape[0] != nbr:
         raise ValueError("outputs have the wrong number of rows")
+    _check_out_shapes(q, s, cols if out_dtype == "e4m3" else cols // 2, nbc if scale_fmt == "f32" else nbc // 4,
+                      scale_fmt)
     _check(tk_per_block_cast(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0), s.data_ptr(),
                              s.stride(0), block_rows, block_cols, QDTYPES[out_dtype], int(bool(round_pow2)),
                              SCALE_FMTS[scale_fmt], _stream_handle(stream, x.device)))
@@ -368,6 +394,8 @@ def per_channel_cast(x: torch.Tensor, out_dtype: str = "e4m3", round_pow2: bool 
         raise ValueError("codes must be 2-D, row-contiguous, on the input's device")
     if s.device != x.device or not s.is_contiguous():
         raise ValueError("scales must be contiguous on the input's device")
+    _check_out_shapes(q, s, cols if out_dtype == "e4m3" else cols // 2, cols if scale_fmt == "f32" else cols // 4,
+                      scale_fmt)
     need = tk_per_channel_workspace_bytes(rows, cols)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=x.device)

@@ -115,7 +115,7 @@ def _ambiguous_rows(cols: int) -> list:
 @pytest.mark.parametrize("cols", [1024, 7168, 16384])
 def test_rmsnorm_exact_path_rows(cols):
     """Rows built on and next to rounding midpoints of the sum of squares,
-    interleaved with ordinary rows (the exact path runs inside the row loop)."""
+    interleaved with ordinary rows."""
     special = np.stack(_ambiguous_rows(cols))
     bits = (special.view(np.uint32) >> 16).astype(np.uint16)
     ordinary = inputs.generate_small(cols, 30, cols, "student_t3")
@@ -123,6 +123,66 @@ def test_rmsnorm_exact_path_rows(cols):
     for out in ("f32", "bf16"):
         check_norm(x, _weight(1, cols), 1e-6, out, label="exact path")
     check_norm_cast(x, None, 1e-6, 128, "e4m3", True, "ue8m0", label="exact path")
+
+
+def _wave_rows():
+    """Rows that the one-wave-per-row kernel's grid takes in one pass (16
+    waves per compute unit); taller inputs run its row loop."""
+    return torch.cuda.get_device_properties(0).multi_processor_count * 16
+
+
+def _looped_input(cols, seed):
+    """2 x (grid rows) + 7 rows, so that every wave converts two or three rows,
+    with the exact-path rows placed in first, second and third passes."""
+    n = _wave_rows()
+    rows = 2 * n + 7
+    x = inputs.generate_small(seed, rows, cols, "student_t3")
+    special = (np.stack(_ambiguous_rows(cols)).view(np.uint32) >> 16).astype(np.uint16)
+    at = [1, n - 1, n, n + 2, 2 * n - 1, 2 * n, 2 * n + 3, 2 * n + 6, n // 2]
+    for i, r in enumerate(at):
+        x[r] = special[i % len(special)]
+    return x
+
+
+@pytest.mark.parametrize("dt,p2,sf", VARIANTS)
+@pytest.mark.parametrize("group", [16, 32, 64, 128])
+def test_rmsnorm_cast_row_loop(dt, p2, sf, group):
+    """Inputs taller than the grid: the row loop, with the next row loaded
+    while the current one is converted, and exact-path rows inside it."""
+    cols = 1024 + 4 * group
+    x = _looped_input(cols, 11 + group)
+    check_norm_cast(x, _weight(group, cols), 1e-6, group, dt, p2, sf, x_ld=cols + 8, label="row loop")
+
+
+@pytest.mark.parametrize("cols,group,dt,p2,sf", [(7168, 128, "e4m3", True, "f32"), (7168, 32, "e2m1", True, "ue8m0"),
+                                                 (4096, 64, "e4m3", True, "ue8m0"), (3584, 16, "e2m1", False, "f32")])
+def test_rmsnorm_cast_row_loop_wide(cols, group, dt, p2, sf):
+    x = _looped_input(cols, 5)
+    check_norm_cast(x, _weight(1, cols), 1e-6, group, dt, p2, sf, label="row loop")
+
+
+@pytest.mark.parametrize("wi", [2, 4])
+def test_rmsnorm_cast_full_size_sampled(wi):
+    """Full-size workloads (16384 and 32768 rows), as the benchmark launches
+    them; the oracle checks a sample of rows (each row is independent): the
+    first and last rows, those around each pass of the grid, and every 97th."""
+    w = inputs.WORKLOADS[wi]
+    x = inputs.generate(w, cache=True)
+    wt = _weight(7, w.cols)
+    log(f"[gpu] rmsnorm-cast full size {w.rows}x{w.cols} G={w.group} {w.out_dtype} {w.scale_fmt}")
+    q, s = tk.rmsnorm_cast(to_dev(x), _wdev(wt), 1e-6, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)
+    torch.cuda.synchronize()
+    n = _wave_rows()
+    pick = set(range(8)) | set(range(w.rows - 8, w.rows)) | set(range(0, w.rows, 97))
+    for k in range(1, w.rows // n + 1):
+        pick |= {r for r in range(k * n - 3, k * n + 3) if 0 <= r < w.rows}
+    idx = np.array(sorted(pick))
+    want_q, want_s = _rows_parallel(
+        lambda xb: oracle.rmsnorm_cast(xb, wt, 1e-6, w.group, w.out_dtype, w.round_pow2, w.scale_fmt), x[idx])
+    got_q = q.cpu().numpy()[idx]
+    got_s = s.cpu().numpy().view(np.uint32)[idx]
+    assert np.array_equal(got_s, want_s.view(np.uint32)), first_mismatch(got_s, want_s.view(np.uint32))
+    assert np.array_equal(got_q, want_q), first_mismatch(got_q, want_q)
 
 
 def test_rmsnorm_zero_rows_and_large_eps():
