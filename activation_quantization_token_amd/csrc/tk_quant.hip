@@ -67,7 +67,8 @@ constexpr int kSiluValues = 2 * int(kSiluHi - kSiluLo + 1);
 constexpr int kSiluEntries = kSiluValues + 2;
 constexpr uint32_t kSentinel = 0x7FC00000u;   // quiet NaN
 
-__device__ float g_silu_table[kSiluEntries];
+__device__ __align__(16) float g_silu_table[kSiluEntries];
+static_assert(kSiluEntries % 4 == 0, "the table is copied in 16-byte pieces");
 
 // Round main + tail (|tail| small against |main|) to the nearest fp32, ties
 // to even, as one rounding of the exact sum.  TwoSum (Knuth) gives s + e ==
@@ -514,10 +515,7 @@ __global__ __launch_bounds__(kStreamBlock) void stream_rw_kernel(const u32x4 *sr
 template <int G, int QD, bool POW2, int SF, int U, int WPB>
 __global__ __launch_bounds__(kWave * WPB) void swiglu_cast_kernel(CastParams p)
 {
-    __shared__ float tab[kSiluEntries];
-    for (int i = threadIdx.x; i < kSiluEntries; i += kWave * WPB) tab[i] = g_silu_table[i];
-    __syncthreads();
-
+    __shared__ __align__(16) float tab[kSiluEntries];
     const int lane = threadIdx.x & (kWave - 1);
     // threadIdx.x >> 6 is the same on every lane of a wave; readfirstlane tells
     // the compiler so, which keeps the row descriptors in scalar registers.
@@ -527,17 +525,45 @@ __global__ __launch_bounds__(kWave * WPB) void swiglu_cast_kernel(CastParams p)
     const int64_t runs = (nseg + U - 1) / U;
     const int64_t units = p.rows * runs;
     const uint32_t half_bytes = uint32_t(p.cols) * 2u;
-    for (int64_t unit = wave; unit < units; unit += nwaves) {
-        const Unit un = decode_unit<U>(unit, runs, lane);
+    u32x4 wg[U], wu[U];
+    auto load_unit = [&](const Unit &un) {
         const uint16_t *grow = p.x + un.row * p.x_ld;
         const __amdgpu_buffer_rsrc_t gate = row_buffer(grow, half_bytes);
         const __amdgpu_buffer_rsrc_t up = row_buffer(grow + p.cols, half_bytes);
-        u32x4 wg[U], wu[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             wg[k] = load16(gate, (un.col0 + k * kSegCols) * 2u);
             wu[k] = load16(up, (un.col0 + k * kSegCols) * 2u);
         }
+    };
+
+    // The wave's first unit is requested before the table is copied; the
+    // copy reads 16-byte pieces, all of a thread's in flight at once.
+    int64_t unit = wave;
+    Unit un{};
+    if (unit < units) {
+        un = decode_unit<U>(unit, runs, lane);
+        load_unit(un);
+    }
+    {
+        constexpr int kPieces = kSiluEntries / 4;
+        constexpr int kPerThread = (kPieces + kWave * WPB - 1) / (kWave * WPB);
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(g_silu_table);
+        u32x4 t[kPerThread];
+#pragma unroll
+        for (int c = 0; c < kPerThread; ++c) {
+            const int i = int(threadIdx.x) + c * kWave * WPB;
+            if (i < kPieces) t[c] = src[i];
+        }
+#pragma unroll
+        for (int c = 0; c < kPerThread; ++c) {
+            const int i = int(threadIdx.x) + c * kWave * WPB;
+            if (i < kPieces) reinterpret_cast<u32x4 *>(tab)[i] = t[c];
+        }
+    }
+    __syncthreads();
+
+    for (; unit < units; ) {
         __amdgpu_buffer_rsrc_t qrow, srow;
         output_rows<G, QD, SF>(p, un.row, qrow, srow);
         Quantized qz[U];
@@ -571,6 +597,11 @@ __global__ __launch_bounds__(kWave * WPB) void swiglu_cast_kernel(CastParams p)
             else store4(qrow, (un.col0 + k * kSegCols) / 2, qz[k].codes.x);
         }
         store_unit_scales<G, SF, U>(qz, lane, un.col0 - uint32_t(lane) * 8u, srow);
+        unit += nwaves;
+        if (unit < units) {
+            un = decode_unit<U>(unit, runs, lane);
+            load_unit(un);
+        }
     }
 }
 

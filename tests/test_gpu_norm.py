@@ -161,6 +161,13 @@ def test_rmsnorm_cast_row_loop_wide(cols, group, dt, p2, sf):
     check_norm_cast(x, _weight(1, cols), 1e-6, group, dt, p2, sf, label="row loop")
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("cols", [1024, 3584, 7168])
+def test_rmsnorm_row_loop(out, cols):
+    x = _looped_input(cols, 3)
+    check_norm(x, _weight(2, cols), 1e-6, out, x_ld=cols + 8, label="row loop")
+
+
 @pytest.mark.parametrize("wi", [2, 4])
 def test_rmsnorm_cast_full_size_sampled(wi):
     """Full-size workloads (16384 and 32768 rows), as the benchmark launches
@@ -205,6 +212,25 @@ def test_rmsnorm_full_size_bf16():
     w = inputs.WORKLOADS[1]
     x = inputs.generate(w, cache=True)
     check_norm(x, _weight(7, w.cols), 1e-6, "bf16", label="4096x7168")
+
+
+def test_rmsnorm_full_size_sampled_bf16():
+    """32768 rows (the benchmark's plain-forward launch); a sample of rows
+    checked by the oracle."""
+    w = inputs.WORKLOADS[4]
+    x = inputs.generate(w, cache=True)
+    wt = _weight(7, w.cols)
+    log(f"[gpu] rmsnorm full size {w.rows}x{w.cols} bf16")
+    y = tk.rmsnorm(to_dev(x), _wdev(wt), 1e-6, "bf16")
+    torch.cuda.synchronize()
+    n = _wave_rows()
+    pick = set(range(8)) | set(range(w.rows - 8, w.rows)) | set(range(0, w.rows, 97))
+    for k in range(1, w.rows // n + 1):
+        pick |= {r for r in range(k * n - 3, k * n + 3) if 0 <= r < w.rows}
+    idx = np.array(sorted(pick))
+    want = _rows_parallel(lambda xb: oracle.rmsnorm(xb, wt, 1e-6, "bf16"), x[idx])
+    got = y.cpu().view(torch.int16).numpy().view(np.uint16)[idx]
+    assert np.array_equal(got, want), first_mismatch(got, want)
 
 
 def test_rmsnorm_cast_equals_cast_of_rmsnorm_output():
