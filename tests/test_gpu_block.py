@@ -136,7 +136,9 @@ def test_per_block_zero_and_extreme_blocks():
         check_block(x, 128, 128, dt, p2, sf, label="zeros/extremes")
 
 
-CHANNEL_SHAPES = [(1, 8), (3, 520), (64, 4096), (130, 7168), (1000, 776), (2049, 64)]
+# Chunk counts from 1 to 32 (64-row chunks up to 2048 rows, 32 chunks above).
+CHANNEL_SHAPES = [(1, 8), (3, 520), (64, 4096), (130, 7168), (1000, 776), (2049, 64), (4096, 1032), (4097, 520),
+                  (5003, 1040)]
 
 
 @pytest.mark.parametrize("dt,p2,sf", VARIANTS)
