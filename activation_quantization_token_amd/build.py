@@ -12,7 +12,8 @@ import sys
 
 PKG = pathlib.Path(__file__).resolve().parent
 ROOT = PKG.parent
-SOURCES = [PKG / "csrc" / "tk_quant.hip", PKG / "csrc" / "tk_block.hip", PKG / "csrc" / "tk_norm.hip"]
+SOURCES = [PKG / "csrc" / "tk_quant.hip", PKG / "csrc" / "tk_block.hip", PKG / "csrc" / "tk_norm.hip",
+           PKG / "csrc" / "tk_diag.hip"]
 INCLUDE = ROOT / "include"
 LIB = PKG / "libtk_quant.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

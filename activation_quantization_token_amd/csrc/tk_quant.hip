@@ -467,51 +467,6 @@ __global__ __launch_bounds__(kSiluBlock) void silu32_kernel(const uint16_t *g, f
     if (i + 1 < n) out[i + 1] = r1;
 }
 
-constexpr int kCopyBlock = 256;
-
-__global__ __launch_bounds__(kCopyBlock) void copy_stream_kernel(const u32x4 *src, u32x4 *dst, int64_t n16)
-{
-    const int64_t stride = int64_t(gridDim.x) * kCopyBlock;
-    for (int64_t i = int64_t(blockIdx.x) * kCopyBlock + threadIdx.x; i < n16; i += stride)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
-}
-
-// A stream of nr 16-byte loads and nw 16-byte stores laid out like the
-// cast's traffic: workgroup c takes chunk c of kStreamChunk units of the
-// larger stream (contiguous, 4 KiB per wave-group instruction) and the
-// proportional contiguous chunk of the smaller one.  All its loads are issued
-// before any store; the loads are folded into a running xor that the stores
-// write, so none can be dropped.  Every unit is loaded once and written once.
-// 16 units per thread, 256 threads (measured best of 1-16 units x 256-1024
-// threads; strides of 4 and 8 units per thread were 10-50 % slower).
-constexpr int kStreamUnits = 16;
-constexpr int kStreamBlock = 256;
-constexpr int kStreamChunk = kStreamUnits * kStreamBlock;
-
-__global__ __launch_bounds__(kStreamBlock) void stream_rw_kernel(const u32x4 *src, int64_t nr, u32x4 *dst, int64_t nw)
-{
-    const int64_t nl = nr > nw ? nr : nw;
-    const int64_t c0 = int64_t(blockIdx.x) * kStreamChunk;
-    const int64_t c1 = c0 + kStreamChunk < nl ? c0 + kStreamChunk : nl;
-    const int64_t r0 = c0 * nr / nl, r1 = c1 * nr / nl;      // exact bounds when nr == nl
-    const int64_t w0 = c0 * nw / nl, w1 = c1 * nw / nl;
-    u32x4 v[kStreamUnits];
-#pragma unroll
-    for (int k = 0; k < kStreamUnits; ++k) {
-        const int64_t i = r0 + int64_t(k) * kStreamBlock + threadIdx.x;
-        v[k] = u32x4{0u, 0u, 0u, 0u};
-        if (i < r1) v[k] = __builtin_nontemporal_load(src + i);
-    }
-    u32x4 acc = v[0];
-#pragma unroll
-    for (int k = 1; k < kStreamUnits; ++k) acc ^= v[k];
-#pragma unroll
-    for (int k = 0; k < kStreamUnits; ++k) {
-        const int64_t j = w0 + int64_t(k) * kStreamBlock + threadIdx.x;
-        if (j < w1) __builtin_nontemporal_store(acc, dst + j);
-    }
-}
-
 template <int G, int QD, bool POW2, int SF, int U, int WPB>
 __global__ __launch_bounds__(kWave * WPB) void swiglu_cast_kernel(CastParams p)
 {
@@ -982,52 +937,6 @@ tk_status tk_silu32_bf16(const void *g, void *out, int64_t n, void *stream)
     if (blocks > int64_t(0x7FFFFFFF)) return TK_ERROR_INVALID_VALUE;
     if (hipLaunchKernel(reinterpret_cast<const void *>(silu32_kernel), dim3(uint32_t(blocks)), dim3(kSiluBlock),
                         args, 0, s) != hipSuccess)
-        return TK_ERROR_LAUNCH;
-    return TK_SUCCESS;
-}
-
-tk_status tk_copy_stream(const void *src, void *dst, int64_t bytes, void *stream)
-{
-    if (bytes < 0 || bytes % 16 != 0) return TK_ERROR_INVALID_VALUE;
-    if (bytes == 0) return TK_SUCCESS;
-    if (!src || !dst) return TK_ERROR_INVALID_VALUE;
-    if (!aligned(src, 16) || !aligned(dst, 16)) return TK_ERROR_MISALIGNED;
-    int dev = 0;
-    DeviceInfo *info = nullptr;
-    tk_status st = device_info(&dev, &info);
-    if (st != TK_SUCCESS) return st;
-    const u32x4 *sp = static_cast<const u32x4 *>(src);
-    u32x4 *dp = static_cast<u32x4 *>(dst);
-    int64_t n16 = bytes / 16;
-    int64_t blocks = (n16 + kCopyBlock - 1) / kCopyBlock;
-    if (blocks > int64_t(info->cus) * 128) blocks = int64_t(info->cus) * 128;
-    void *args[] = {&sp, &dp, &n16};
-    if (hipLaunchKernel(reinterpret_cast<const void *>(copy_stream_kernel), dim3(uint32_t(blocks)),
-                        dim3(kCopyBlock), args, 0, static_cast<hipStream_t>(stream)) != hipSuccess)
-        return TK_ERROR_LAUNCH;
-    return TK_SUCCESS;
-}
-
-tk_status tk_stream_rw(const void *src, int64_t read_bytes, void *dst, int64_t write_bytes, void *stream)
-{
-    if (read_bytes < 0 || write_bytes < 0 || read_bytes % 16 != 0 || write_bytes % 16 != 0)
-        return TK_ERROR_INVALID_VALUE;
-    if (read_bytes >= (int64_t(1) << 35) || write_bytes >= (int64_t(1) << 35))
-        return TK_ERROR_UNSUPPORTED;                      // chunk bounds c * n stay within int64
-    if (read_bytes == 0 || write_bytes == 0) return read_bytes == write_bytes ? TK_SUCCESS : TK_ERROR_INVALID_VALUE;
-    if (!src || !dst) return TK_ERROR_INVALID_VALUE;
-    if (!aligned(src, 16) || !aligned(dst, 16)) return TK_ERROR_MISALIGNED;
-    int dev = 0;
-    DeviceInfo *info = nullptr;
-    tk_status st = device_info(&dev, &info);
-    if (st != TK_SUCCESS) return st;
-    const u32x4 *sp = static_cast<const u32x4 *>(src);
-    u32x4 *dp = static_cast<u32x4 *>(dst);
-    int64_t nr = read_bytes / 16, nw = write_bytes / 16;
-    const int64_t blocks = ((nr > nw ? nr : nw) + kStreamChunk - 1) / kStreamChunk;
-    void *args[] = {&sp, &nr, &dp, &nw};
-    if (hipLaunchKernel(reinterpret_cast<const void *>(stream_rw_kernel), dim3(uint32_t(blocks)), dim3(kStreamBlock),
-                        args, 0, static_cast<hipStream_t>(stream)) != hipSuccess)
         return TK_ERROR_LAUNCH;
     return TK_SUCCESS;
 }

@@ -270,10 +270,11 @@ tk_status tk_copy_stream(const void *src, void *dst, int64_t bytes, void *stream
 
 /*
  * tk_stream_rw -- diagnostic: read `read_bytes` from src and write
- * `write_bytes` to dst with the cast's memory instructions (16-byte
- * non-temporal loads and stores), each workgroup reading a contiguous 64 KiB
- * of the larger stream and the proportional contiguous piece of the other.  The written values are a running xor of what was read (every
- * load is kept); their contents are otherwise meaningless.  Used as the
+ * `write_bytes` to dst with the row-form cast's memory instructions and
+ * shape (non-temporal 16-byte loads, 4-byte stores per lane; workgroups of 7
+ * waves, each wave reading 2 KiB and writing an equal share of dst).  The
+ * written values are an xor of what was read (every load is kept); their
+ * contents are otherwise meaningless.  Used as the
  * practical streaming ceiling of an operation with the same read and write
  * volumes.  Sizes multiples of 16, both nonzero (or both zero: nothing to
  * do), pointers 16-byte aligned (TK_ERROR_INVALID_VALUE /

@@ -60,7 +60,7 @@ def objects(tmp_path_factory):
         path = d / f"module{k}.o"
         path.write_bytes(co)
         paths.append(path)
-    assert len(paths) == 3, "one code object per HIP source expected"
+    assert len(paths) == 4, "one code object per HIP source expected"
     return paths
 
 
