@@ -111,6 +111,11 @@ def _oracle_step(op: str, w, block, weight_bits):
     if op == "cast":
         fn = oracle.swiglu_per_token_cast if w.swiglu else oracle.per_token_cast
         return (lambda xs: fn(xs, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)), 1, w.algorithmic_bytes(1)
+    if op == "cast_f32":
+        def run(xs):
+            xf = (xs.astype(np.uint32) << 16).view(np.float32)        # the bench's fp32 input: bf16 widened
+            oracle.per_token_cast_f32(xf, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)
+        return run, 1, 4 * w.cols + code_cols + 4 * w.scale_cols
     if op == "dequant":
         def run(xs):
             q, s = oracle.per_token_cast(xs, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)
@@ -197,8 +202,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed steps; HBM and fabric clocks need ~15 ms of sustained load to settle")
     ap.add_argument("--workload", type=int, default=4)
-    ap.add_argument("--op", choices=["cast", "dequant", "cast_back", "per_block", "per_channel", "rmsnorm", "rmsnorm_cast"], default="cast",
-                    help="cast (the workload's cast, fused SwiGLU for workload 3), its dequantization, "
+    ap.add_argument("--op", choices=["cast", "cast_f32", "dequant", "cast_back", "per_block", "per_channel", "rmsnorm",
+                                     "rmsnorm_cast"], default="cast",
+                    help="cast (the workload's cast, fused SwiGLU for workload 3), the same cast of the "
+                         "input widened to fp32, its dequantization, "
                          "the fused cast-and-cast-back, the per-block / per-channel cast of the "
                          "workload's input with its code and scale formats, RMSNorm forward (bf16 out) "
                          "or RMSNorm fused with the workload's per-token cast")
@@ -249,6 +256,14 @@ def main():
             fn(xi, w.group, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si))
         nbytes = w.algorithmic_bytes()
         read_bytes = w.rows * w.in_cols * 2
+    elif args.op == "cast_f32":
+        # the workload's input widened to fp32 (exact), cast with the fp32-input kernel
+        sets = [(xi.float(), qi, si) for (xi, qi, si) in sets]
+
+        def run(xi, qi, si, yi):
+            tk.per_token_cast(xi, w.group, w.out_dtype, w.round_pow2, w.scale_fmt, out=(qi, si))
+        nbytes = w.rows * (4 * w.cols + w.code_cols + 4 * w.scale_cols)
+        read_bytes = w.rows * 4 * w.cols
     elif args.op == "dequant":
         # inputs: the workload's codes and scales (made by the cast); output bf16
         for i in range(len(sets)):

@@ -315,7 +315,7 @@ def test_very_wide_rows(group, dt, p2, sf, cols):
 
 @pytest.mark.parametrize("group,dt,p2,sf", [(g, dt, p2, sf) for g in (16, 32, 64, 128) for dt in ("e4m3", "e2m1")
                                           for p2, sf in VARIANTS])
-@pytest.mark.parametrize("rows,extra", [(3, None), (129, 512)])
+@pytest.mark.parametrize("rows,extra", [(3, None), (129, 512), (4099, 512)])   # 4 and 2 pieces per wave
 def test_fp32_input_cast(group, dt, p2, sf, rows, extra):
     cols = 7168 if extra is None else extra + 4 * group
     x = inputs.generate_small_f32(rows + group, rows, cols)
@@ -333,3 +333,23 @@ def test_fp32_input_cast(group, dt, p2, sf, rows, extra):
     got_q, got_s = q.view.cpu().numpy(), s.view.cpu().numpy()
     assert np.array_equal(got_q, wq), first_mismatch(got_q, wq)
     assert np.array_equal(got_s.view(np.uint32), ws.view(np.uint32))
+
+
+@pytest.mark.parametrize("wi", [1, 4])
+def test_fp32_input_cast_full_size_sampled(wi):
+    """The workload's input widened to fp32 (exact), cast at full size as the
+    benchmark's fp32 operation launches it; the oracle checks a sample of rows
+    (the first and last 8 and every 97th)."""
+    w = inputs.WORKLOADS[wi]
+    xb = inputs.generate(w, cache=True)
+    log(f"[gpu] fp32-input cast full size {w.rows}x{w.cols} G={w.group} {w.out_dtype} {w.scale_fmt}")
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda().float()
+    q, s = tk.per_token_cast(x, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)
+    torch.cuda.synchronize()
+    idx = np.array(sorted(set(range(8)) | set(range(w.rows - 8, w.rows)) | set(range(0, w.rows, 97))))
+    xf = (xb[idx].astype(np.uint32) << 16).view(np.float32)
+    wq, ws = oracle.per_token_cast_f32(xf, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)
+    got_q = q.cpu().numpy()[idx]
+    got_s = s.cpu().numpy().view(np.uint32)[idx]
+    assert np.array_equal(got_q, wq), first_mismatch(got_q, wq)
+    assert np.array_equal(got_s, ws.view(np.uint32)), first_mismatch(got_s, ws.view(np.uint32))
