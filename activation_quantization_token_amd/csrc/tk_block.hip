@@ -137,7 +137,7 @@ constexpr bool kChannelReverse = TK_CHANNEL_REVERSE != 0;
 #endif
 constexpr int kChannelFirstPassPolicy = TK_CHANNEL_P1_POLICY;
 constexpr int64_t kChannelMinChunkRows = 64;
-constexpr int64_t kInfinityCacheBytes = int64_t(256) << 20;
+constexpr int64_t kChannelCachedBytes = int64_t(128) << 20;   // half the 256 MiB Infinity Cache
 constexpr int64_t kChannelMaxChunks = 32;
 static_assert(kChannelMaxChunks % kChannelWPB == 0, "each wave reduces the same number of chunks");
 
@@ -250,8 +250,8 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_amax_kernel(Chann
 // Pass 2: the stripe's scales from the chunk maxima, then codes against the
 // column scales.  The first batch of rows is loaded before the chunk maxima
 // are reduced, so their latencies overlap.  P2_POLICY: the loads' cache
-// policy (ordinary when x fits in the Infinity Cache, where the first pass
-// left it; non-temporal otherwise).
+// policy (ordinary when x is small enough to stay in the Infinity Cache,
+// where the first pass left it; non-temporal otherwise).
 template <int QD, bool POW2, int SF, int P2_POLICY>
 __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(ChannelParams p)
 {
@@ -528,10 +528,11 @@ tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t
     if (hipLaunchKernel(reinterpret_cast<const void *>(channel_amax_kernel), dim3(uint32_t(tiles)),
                         dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
         return TK_ERROR_LAUNCH;
-    // Second pass: ordinary loads while x fits in the 256 MiB Infinity Cache
-    // (measured -5 % at 4096 x 7168 and -7 % at 16384 x 7168), non-temporal
-    // beyond (-7 % at 32768 x 7168).
-    const int pi = rows * cols * 2 <= kInfinityCacheBytes ? 1 : 0;
+    // Second pass: ordinary loads while x takes at most half the 256 MiB
+    // Infinity Cache (measured with inputs rotated over three buffer sets:
+    // -6 % at 4096 x 7168; at 16384 x 7168, 235 MB, ordinary loads were 4 %
+    // slower), non-temporal beyond.
+    const int pi = rows * cols * 2 <= kChannelCachedBytes ? 1 : 0;
     if (hipLaunchKernel(reinterpret_cast<const void *>(table.cast[out_dtype][variant][pi]), dim3(uint32_t(tiles)),
                         dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
         return TK_ERROR_LAUNCH;
