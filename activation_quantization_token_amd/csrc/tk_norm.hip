@@ -482,13 +482,15 @@ __device__ __forceinline__ int64_t uniform64(int64_t v)
                    uint32_t(__builtin_amdgcn_readfirstlane(int(v))));
 }
 
-// ONE_ROW: the grid has a wave for every row, so each wave converts one row
-// and, with no next row to load, keeps the row's codes in registers and
-// stores them together at the end (measured 9 % faster at 4096 x 7168 than
-// storing each segment's codes as it is converted).  Otherwise each wave
-// runs its own row loop (rows wave_id, wave_id + total waves, ...) and loads
-// the next row's segment k into the registers the cast has just freed.
-template <int G, int QD, bool POW2, int SF, int OUT, int NS, bool ONE_ROW>
+// The grid has a wave for every row (up to 2^31 - 1 workgroups of 4; taller
+// inputs loop, wave w taking rows w, w + total waves, ...), workgroups
+// dispatched in row order, so the rows in flight form one compact window as
+// in the row-form cast.  A wave keeps its row's codes in registers and stores
+// them together after the row is converted.  Measured against a persistent
+// grid of 16 waves per CU whose waves load their next row into the registers
+// the cast frees: 7 % faster at 32768 x 7168, 2 % at 16384; storing each
+// segment's codes as it is converted: 9 % slower at 4096 x 7168.
+template <int G, int QD, bool POW2, int SF, int OUT, int NS>
 __global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void rmsnorm_wave_kernel(NormParams p)
 {
     static_assert(OUT == kOutCast, "the one-wave-per-row kernel serves the fused cast");
@@ -506,15 +508,15 @@ __global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void r
     // loads go out before the weight row is staged.
     const int64_t nwaves = int64_t(gridDim.x) * kNormWaveWPB;
     int64_t row = uniform64(int64_t(blockIdx.x) * kNormWaveWPB + wave);
-    const bool active = row < p.rows;
     const uint32_t q_bytes = QD == kE4M3 ? cols : cols / 2;
     u32x4 xs[NS];
-    if (active) {
-        const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + row * p.x_ld, cols * 2u);
+    auto load_row = [&](int64_t r) {
+        const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + r * p.x_ld, cols * 2u);
 #pragma unroll
         for (int k = 0; k < NS; ++k)
             xs[k] = __builtin_amdgcn_raw_buffer_load_b128(xrow, int(lane * 16), k * kSegCols * 2, kNonTemporal);
-    }
+    };
+    if (row < p.rows) load_row(row);
 
     // Weight row into LDS as fp32 (w_j, or 1.0 without a weight; 0 past the
     // row end), read in 16-byte pieces that are all in flight at once.
@@ -544,8 +546,9 @@ __global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void r
         }
     }
     __syncthreads();                              // the only workgroup barrier
-    if (!active) return;
-    if constexpr (ONE_ROW) {
+
+    for (bool first = true; row < p.rows; row = uniform64(row + nwaves), first = false) {
+        if (!first) load_row(row);
         const float r = row_inv_rms<NS>(xs, exact_acc[wave], lane, cols_f, p.eps);
         const __amdgpu_buffer_rsrc_t qrow = row_buffer(static_cast<uint8_t *>(p.out) + row * p.out_ld, q_bytes);
         u32x2 codes[NS];
@@ -560,25 +563,6 @@ __global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void r
 #pragma unroll
         for (int k = 0; k < NS; ++k) store_codes<QD>(qrow, lane, k, codes[k]);
         store_row_scales<G, SF>(p, row, cols, lane, stage[wave]);
-    } else {
-        // rows this wave converts (a count, so that the loop test is a 32-bit scalar compare)
-        const int nrows = __builtin_amdgcn_readfirstlane(int((p.rows - row + nwaves - 1) / nwaves));
-        for (int it = 0; it < nrows; ++it, row = uniform64(row + nwaves)) {
-            const bool has_next = it + 1 < nrows;
-            const __amdgpu_buffer_rsrc_t nrow = row_buffer(p.x + (row + (has_next ? nwaves : 0)) * p.x_ld, cols * 2u);
-            const float r = row_inv_rms<NS>(xs, exact_acc[wave], lane, cols_f, p.eps);
-            const __amdgpu_buffer_rsrc_t qrow = row_buffer(static_cast<uint8_t *>(p.out) + row * p.out_ld, q_bytes);
-#pragma unroll
-            for (int k = 0; k < NS; ++k) {
-                const uint32_t col = uint32_t(k) * kSegCols + uint32_t(lane) * 8u;
-                const Quantized qz = norm_segment<G, QD, POW2>(xs[k], r, lds_weight, col);
-                if (has_next)           // the next row's segment k takes this one's registers
-                    xs[k] = __builtin_amdgcn_raw_buffer_load_b128(nrow, int(lane * 16), k * kSegCols * 2, kNonTemporal);
-                store_codes<QD>(qrow, lane, k, qz.codes);
-                stage_scales<G, SF>(qz, col, cols, lane, stage[wave]);
-            }
-            store_row_scales<G, SF>(p, row, cols, lane, stage[wave]);
-        }
     }
 }
 
@@ -590,7 +574,7 @@ using NormFn = void (*)(NormParams);
 constexpr int kWaveNS[3] = {4, 8, 14};
 
 struct NormTable {
-    NormFn cast[7][4][2][3];     // [kernel: workgroup, NS 4/8/14 row loop, NS 4/8/14 one row][group][code format][variant]
+    NormFn cast[4][4][2][3];     // [kernel: workgroup, one wave per row with NS 4/8/14][group][code format][variant]
     NormFn plain[2];             // [bf16 y, fp32 y], workgroup-per-row kernel
 };
 
@@ -598,12 +582,9 @@ template <int G, int QD, bool POW2, int SF>
 void fill_norm_variant(NormTable &t, int gi, int vi)
 {
     t.cast[0][gi][QD][vi] = rmsnorm_kernel<G, QD, POW2, SF, kOutCast>;
-    t.cast[1][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 4, false>;
-    t.cast[2][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 8, false>;
-    t.cast[3][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 14, false>;
-    t.cast[4][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 4, true>;
-    t.cast[5][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 8, true>;
-    t.cast[6][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 14, true>;
+    t.cast[1][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 4>;
+    t.cast[2][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 8>;
+    t.cast[3][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 14>;
 }
 
 template <int G, int QD>
@@ -642,9 +623,6 @@ tk_status validate_norm(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
 #ifndef TK_NORM_WAVES_PER_CU
 #define TK_NORM_WAVES_PER_CU 32
 #endif
-#ifndef TK_NORM_WAVE_WAVES_PER_CU
-#define TK_NORM_WAVE_WAVES_PER_CU 16
-#endif
 
 // 0: workgroup-per-row kernel; 1..3: one wave per row holding 4/8/14 segments.
 int norm_kernel_index(int64_t cols)
@@ -663,11 +641,9 @@ tk_status launch_norm(const NormTable &t, int gi, int qd, int variant, int plain
     // kernel at every width; the fused cast with one wave per row.
     const int ki = plain >= 0 ? 0 : norm_kernel_index(p.cols);
     if (ki > 0) {
-        int64_t blocks = int64_t(cus) * (TK_NORM_WAVE_WAVES_PER_CU / kNormWaveWPB);
-        const int64_t need = (p.rows + kNormWaveWPB - 1) / kNormWaveWPB;
-        const bool one_row = need <= blocks;          // a wave for every row
-        if (one_row) blocks = need;
-        const NormFn fn = t.cast[one_row ? ki + 3 : ki][gi][qd][variant];
+        int64_t blocks = (p.rows + kNormWaveWPB - 1) / kNormWaveWPB;    // a wave for every row
+        if (blocks > int64_t(0x7FFFFFFF)) blocks = int64_t(0x7FFFFFFF);  // taller inputs loop
+        const NormFn fn = t.cast[ki][gi][qd][variant];
         const size_t lds = size_t(kWaveNS[ki - 1]) * kSegCols * 4u;      // fp32 weight row
         if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * kNormWaveWPB),
                             args, lds, s) != hipSuccess)

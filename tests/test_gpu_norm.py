@@ -126,14 +126,14 @@ def test_rmsnorm_exact_path_rows(cols):
 
 
 def _wave_rows():
-    """Rows that the one-wave-per-row kernel's grid takes in one pass (16
-    waves per compute unit); taller inputs run its row loop."""
+    """A row count to place test rows around (16 waves per compute unit)."""
     return torch.cuda.get_device_properties(0).multi_processor_count * 16
 
 
 def _looped_input(cols, seed):
-    """2 x (grid rows) + 7 rows, so that every wave converts two or three rows,
-    with the exact-path rows placed in first, second and third passes."""
+    """A tall input (2 x 4096 + 7 rows on 256 CUs) with exact-path rows placed
+    at its start, middle and end and around multiples of the row count of
+    16 waves per CU."""
     n = _wave_rows()
     rows = 2 * n + 7
     x = inputs.generate_small(seed, rows, cols, "student_t3")
@@ -146,33 +146,33 @@ def _looped_input(cols, seed):
 
 @pytest.mark.parametrize("dt,p2,sf", VARIANTS)
 @pytest.mark.parametrize("group", [16, 32, 64, 128])
-def test_rmsnorm_cast_row_loop(dt, p2, sf, group):
-    """Inputs taller than the grid: the row loop, with the next row loaded
-    while the current one is converted, and exact-path rows inside it."""
+def test_rmsnorm_cast_tall_inputs(dt, p2, sf, group):
+    """Tall inputs (thousands of workgroups, rows of 1088 to 1536 channels)
+    with exact-path rows among them."""
     cols = 1024 + 4 * group
     x = _looped_input(cols, 11 + group)
-    check_norm_cast(x, _weight(group, cols), 1e-6, group, dt, p2, sf, x_ld=cols + 8, label="row loop")
+    check_norm_cast(x, _weight(group, cols), 1e-6, group, dt, p2, sf, x_ld=cols + 8, label="tall")
 
 
 @pytest.mark.parametrize("cols,group,dt,p2,sf", [(7168, 128, "e4m3", True, "f32"), (7168, 32, "e2m1", True, "ue8m0"),
                                                  (4096, 64, "e4m3", True, "ue8m0"), (3584, 16, "e2m1", False, "f32")])
-def test_rmsnorm_cast_row_loop_wide(cols, group, dt, p2, sf):
+def test_rmsnorm_cast_tall_inputs_wide(cols, group, dt, p2, sf):
     x = _looped_input(cols, 5)
-    check_norm_cast(x, _weight(1, cols), 1e-6, group, dt, p2, sf, label="row loop")
+    check_norm_cast(x, _weight(1, cols), 1e-6, group, dt, p2, sf, label="tall")
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("cols", [1024, 3584, 7168])
-def test_rmsnorm_row_loop(out, cols):
+def test_rmsnorm_tall_inputs(out, cols):
     x = _looped_input(cols, 3)
-    check_norm(x, _weight(2, cols), 1e-6, out, x_ld=cols + 8, label="row loop")
+    check_norm(x, _weight(2, cols), 1e-6, out, x_ld=cols + 8, label="tall")
 
 
 @pytest.mark.parametrize("wi", [2, 4])
 def test_rmsnorm_cast_full_size_sampled(wi):
     """Full-size workloads (16384 and 32768 rows), as the benchmark launches
     them; the oracle checks a sample of rows (each row is independent): the
-    first and last rows, those around each pass of the grid, and every 97th."""
+    first and last rows, those around multiples of 4096, and every 97th."""
     w = inputs.WORKLOADS[wi]
     x = inputs.generate(w, cache=True)
     wt = _weight(7, w.cols)
