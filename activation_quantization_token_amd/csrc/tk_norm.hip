@@ -3,8 +3,9 @@
 // 2.0.0: RMSNorm forward with an optional fused FP8 cast).  The arithmetic
 // contract is written out in include/tk_quant.h.
 //
-// Design.  The fused cast of rows of up to 7168 channels runs one row per
-// wave (rmsnorm_wave_kernel below).  Otherwise a workgroup owns one row at a
+// Design.  Rows of up to 7168 channels run one row per wave
+// (rmsnorm_wave_kernel below), for the fused cast and the plain forward
+// alike.  Wider rows: a workgroup owns one row at a
 // time (a persistent grid strides over the rows, each workgroup prefetching
 // its next row) and holds the whole row in registers: W = ceil(cols / 1024)
 // waves, each lane 2 segments of 8 bf16 (16-byte loads, 1 KiB per wave
@@ -475,6 +476,34 @@ __device__ __forceinline__ void store_row_scales(const NormParams &p, int64_t ro
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
+// Segment k of a row of the plain forward: y = (x * r) * w stored as bf16 or
+// fp32 with 16-byte stores whose offset lies wholly in the vector offset
+// (the scalar offset is zero): for a 16-byte buffer store with a register in
+// the scalar-offset field the compiler inserts no wait state before a VALU
+// write of the stored registers, and on gfx950 such a write right after the
+// store was seen to change the stored data.
+template <int OUT>
+__device__ __forceinline__ void norm_segment_out(const NormParams &p, int64_t row, uint32_t cols, const u32x4 &xk,
+                                                 float r, const float *lds_weight, int lane, int k)
+{
+    const uint32_t col = uint32_t(k) * kSegCols + uint32_t(lane) * 8u;
+    float x[8], y[8], wf[8];
+    widen8(xk, x);
+    weight8(lds_weight, col, wf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = (x[i] * r) * wf[i];
+    if constexpr (OUT == kOutBF16) {
+        const __amdgpu_buffer_rsrc_t yrow = row_buffer(static_cast<uint16_t *>(p.out) + row * p.out_ld, cols * 2u);
+        store16(yrow, col * 2u, pack_bf16x8(y));
+    } else {
+        const __amdgpu_buffer_rsrc_t yrow = row_buffer(static_cast<float *>(p.out) + row * p.out_ld, cols * 4u);
+        store16(yrow, col * 4u, u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                                      __float_as_uint(y[3])});
+        store16(yrow, col * 4u + 16u, u32x4{__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]),
+                                            __float_as_uint(y[7])});
+    }
+}
+
 // The same value on every lane: keeps row indices and descriptors in scalar registers.
 __device__ __forceinline__ int64_t uniform64(int64_t v)
 {
@@ -493,7 +522,6 @@ __device__ __forceinline__ int64_t uniform64(int64_t v)
 template <int G, int QD, bool POW2, int SF, int OUT, int NS>
 __global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void rmsnorm_wave_kernel(NormParams p)
 {
-    static_assert(OUT == kOutCast, "the one-wave-per-row kernel serves the fused cast");
     constexpr int kCols = NS * kSegCols;
     extern __shared__ float lds_weight[];                                 // fp32 [NS * 512]
     __shared__ uint32_t stage[kNormWaveWPB][kCols / 16];
@@ -550,6 +578,11 @@ __global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void r
     for (bool first = true; row < p.rows; row = uniform64(row + nwaves), first = false) {
         if (!first) load_row(row);
         const float r = row_inv_rms<NS>(xs, exact_acc[wave], lane, cols_f, p.eps);
+        if constexpr (OUT != kOutCast) {          // plain forward: each segment's y leaves at once
+#pragma unroll
+            for (int k = 0; k < NS; ++k) norm_segment_out<OUT>(p, row, cols, xs[k], r, lds_weight, lane, k);
+            continue;
+        }
         const __amdgpu_buffer_rsrc_t qrow = row_buffer(static_cast<uint8_t *>(p.out) + row * p.out_ld, q_bytes);
         u32x2 codes[NS];
 #pragma unroll
@@ -575,7 +608,7 @@ constexpr int kWaveNS[3] = {4, 8, 14};
 
 struct NormTable {
     NormFn cast[4][4][2][3];     // [kernel: workgroup, one wave per row with NS 4/8/14][group][code format][variant]
-    NormFn plain[2];             // [bf16 y, fp32 y], workgroup-per-row kernel
+    NormFn plain[4][2];          // [the same kernels][bf16 y, fp32 y]
 };
 
 template <int G, int QD, bool POW2, int SF>
@@ -603,8 +636,14 @@ NormTable make_norm_table()
     fill_norm<32, kE4M3>(t, 1);  fill_norm<32, kE2M1>(t, 1);
     fill_norm<64, kE4M3>(t, 2);  fill_norm<64, kE2M1>(t, 2);
     fill_norm<128, kE4M3>(t, 3); fill_norm<128, kE2M1>(t, 3);
-    t.plain[0] = rmsnorm_kernel<16, kE4M3, false, kScaleF32, kOutBF16>;
-    t.plain[1] = rmsnorm_kernel<16, kE4M3, false, kScaleF32, kOutF32>;
+    t.plain[0][0] = rmsnorm_kernel<16, kE4M3, false, kScaleF32, kOutBF16>;
+    t.plain[0][1] = rmsnorm_kernel<16, kE4M3, false, kScaleF32, kOutF32>;
+    t.plain[1][0] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutBF16, 4>;
+    t.plain[1][1] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutF32, 4>;
+    t.plain[2][0] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutBF16, 8>;
+    t.plain[2][1] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutF32, 8>;
+    t.plain[3][0] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutBF16, 14>;
+    t.plain[3][1] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutF32, 14>;
     return t;
 }
 
@@ -637,20 +676,21 @@ tk_status launch_norm(const NormTable &t, int gi, int qd, int variant, int plain
 {
     NormParams q = p;
     void *args[] = {&q};
-    // The plain forward (y written) measured faster with the workgroup-per-row
-    // kernel at every width; the fused cast with one wave per row.
-    const int ki = plain >= 0 ? 0 : norm_kernel_index(p.cols);
+    // Rows of up to 7168 channels: one wave per row (plain forward measured
+    // 6 % faster than the workgroup kernel at 32768 x 7168, 3 % at 4096);
+    // wider rows: one workgroup per row.
+    const int ki = norm_kernel_index(p.cols);
     if (ki > 0) {
         int64_t blocks = (p.rows + kNormWaveWPB - 1) / kNormWaveWPB;    // a wave for every row
         if (blocks > int64_t(0x7FFFFFFF)) blocks = int64_t(0x7FFFFFFF);  // taller inputs loop
-        const NormFn fn = t.cast[ki][gi][qd][variant];
+        const NormFn fn = plain >= 0 ? t.plain[ki][plain] : t.cast[ki][gi][qd][variant];
         const size_t lds = size_t(kWaveNS[ki - 1]) * kSegCols * 4u;      // fp32 weight row
         if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * kNormWaveWPB),
                             args, lds, s) != hipSuccess)
             return TK_ERROR_LAUNCH;
         return TK_SUCCESS;
     }
-    const NormFn fn = plain >= 0 ? t.plain[plain] : t.cast[0][gi][qd][variant];
+    const NormFn fn = plain >= 0 ? t.plain[0][plain] : t.cast[0][gi][qd][variant];
     const int waves = int((p.cols + kNormU * kSegCols - 1) / (kNormU * kSegCols));
     int64_t per_cu = TK_NORM_WAVES_PER_CU / waves;
     if (per_cu < 1) per_cu = 1;
