@@ -1035,7 +1035,7 @@ const char *tk_status_string(int32_t status)
     switch (status) {
     case TK_SUCCESS: return "TK_SUCCESS";
     case TK_ERROR_INVALID_VALUE: return "TK_ERROR_INVALID_VALUE: invalid size, group, format or null pointer";
-    case TK_ERROR_UNSUPPORTED: return "TK_ERROR_UNSUPPORTED: request not provided by this build";
+    case TK_ERROR_UNSUPPORTED: return "TK_ERROR_UNSUPPORTED: request not provided by this library";
     case TK_ERROR_MISALIGNED: return "TK_ERROR_MISALIGNED: pointer or row stride breaks the alignment rule";
     case TK_ERROR_LAUNCH: return "TK_ERROR_LAUNCH: the HIP runtime refused the kernel launch";
     case TK_ERROR_DEVICE: return "TK_ERROR_DEVICE: no usable gfx950 device";

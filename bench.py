@@ -226,7 +226,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the cast is row-parallel with no exchange between GPUs, "
-              "and this build runs on a single GPU only (--gpus 1).", file=sys.stderr)
+              "and this benchmark runs on a single GPU only (--gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

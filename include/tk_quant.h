@@ -54,7 +54,7 @@ extern "C" {
 typedef enum tk_status {
     TK_SUCCESS = 0,
     TK_ERROR_INVALID_VALUE = 1, /* bad size, group, format or null pointer         */
-    TK_ERROR_UNSUPPORTED = 2,   /* valid request that this build does not provide   */
+    TK_ERROR_UNSUPPORTED = 2,   /* valid request this library does not provide     */
     TK_ERROR_MISALIGNED = 3,    /* a pointer or row stride breaks the alignment rule */
     TK_ERROR_LAUNCH = 4,        /* the HIP runtime refused the launch               */
     TK_ERROR_DEVICE = 5         /* no usable gfx950 device / runtime error          */

@@ -17,7 +17,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests need a GPU; outside a GPU machine they are reported as skipped
+    # GPU tests need a GPU; on a machine without one they are reported as skipped
     # rather than silently passing.
     try:
         import torch
