@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kWave * kMaxBlockWaves) void block_cast_kernel(Bloc
             float x[8], v[8];
             widen8(w[k], x);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = scaled<QD, POW2>(x[i], sc.s, sc.inv);
+            for (int i = 0; i < 8; ++i) v[i] = scaled<QD, POW2, kApplyMul>(x[i], sc.s, sc.inv);
             const u32x2 codes = encode8<QD>(v);
             const uint32_t qbytes = QD == kE4M3 ? cols : cols / 2;
             const __amdgpu_buffer_rsrc_t qrow = row_buffer(p.q + (wr0 + k) * p.q_ld, qbytes);
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(Chann
                 float x[8], v[8];
                 widen8(w[k], x);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = scaled<QD, POW2>(x[i], s[i], inv[i]);
+                for (int i = 0; i < 8; ++i) v[i] = scaled<QD, POW2, kApplyMul>(x[i], s[i], inv[i]);
                 const u32x2 codes = encode8<QD>(v);
                 const __amdgpu_buffer_rsrc_t qrow = row_buffer(p.q + row * p.q_ld, qbytes);
                 if constexpr (QD == kE4M3) store8(qrow, col, codes);

@@ -138,13 +138,30 @@ __device__ __forceinline__ Scale<QD, POW2> group_scale(uint32_t amax_bits)
     return r;
 }
 
-// x / s, clamped to the format's range.  With a power-of-two scale x * 2^-e
-// is the exact quotient x / 2^e rounded once, as x / s is.
-template <int QD, bool POW2>
+// How a scale reaches the converter.  A quotient x / s by IEEE division is
+// clamped to [-D, D]: fl32(a / D) may lie below a / D, so |x| / s can pass D
+// by a rounding.  A power-of-two scale s = 2^e is at least a / D (fl32(a / D)
+// is a power of two only when a / D is one, group_scale), so every |x| <= a
+// gives |x| * 2^-e <= D and rounding cannot pass D either: a clamp there
+// never binds.  Then x * 2^-e, the exact quotient x / 2^e rounded once as
+// x / s is, goes to the converter as it is (kApplyMul), or x goes to the
+// gfx950 scaled converters with s (kApplyScaledCvt: they divide by a
+// power-of-two scale exactly and round once to nearest even, which the fused
+// RMSNorm cast's parity tests check on every code value, midpoint and
+// subnormal code at 26 scales).  kApplyClamp clamps power-of-two quotients
+// too.  Measured on MI355X against kApplyClamp: SwiGLU + cast 1.9 % and the
+// per-block cast 1.3-2.6 % faster with kApplyMul, RMSNorm + cast 3.1 % with
+// kApplyScaledCvt; the plain bf16 cast, a memory-bound stream, 0.7 % slower
+// without the clamp (an effect on the timing of its memory traffic), so it
+// keeps kApplyClamp, as do the fp32-input cast and the cast-and-cast-back.
+enum ApplyMode { kApplyClamp = 0, kApplyMul = 1, kApplyScaledCvt = 2 };
+
+template <int QD, bool POW2, int MODE>
 __device__ __forceinline__ float scaled(float x, float s, float inv)
 {
     constexpr float D = (QD == kE4M3) ? 448.0f : 6.0f;
-    return __builtin_amdgcn_fmed3f(POW2 ? x * inv : x / s, D, -D);
+    if constexpr (POW2 && MODE != kApplyClamp) return x * inv;
+    else return __builtin_amdgcn_fmed3f(POW2 ? x * inv : x / s, D, -D);
 }
 
 // 8 clamped values -> codes, nearest with ties to even, by the gfx950
@@ -168,19 +185,45 @@ __device__ __forceinline__ u32x2 encode8(const float (&v)[8])
     }
 }
 
+// 8 values and their power-of-two scale s -> codes, by the scaled converters
+// (x / s, nearest with ties to even; same packing as encode8).
+template <int QD>
+__device__ __forceinline__ u32x2 encode8_pow2(const float (&x)[8], float s)
+{
+    if constexpr (QD == kE4M3) {
+        typedef short s16x2 __attribute__((ext_vector_type(2)));
+        s16x2 lo = {0, 0}, hi = {0, 0};
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x[0], x[1], s, false);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x[2], x[3], s, true);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, x[4], x[5], s, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, x[6], x[7], s, true);
+        return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    } else {
+        uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0], x[1], s, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[2], x[3], s, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[4], x[5], s, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[6], x[7], s, 3);
+        return u32x2{r, 0u};
+    }
+}
+
 // 8 values whose scale group has |max| bits amax_bits (already reduced over
 // the group) -> codes and scale.
-template <int QD, bool POW2>
+template <int QD, bool POW2, int MODE>
 __device__ __forceinline__ Quantized quantize_values(const float (&x)[8], uint32_t amax_bits)
 {
     const Scale<QD, POW2> sc = group_scale<QD, POW2>(amax_bits);
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = scaled<QD, POW2>(x[i], sc.s, sc.inv);
     Quantized out;
     out.s = sc.s;
     out.e8 = sc.e8;
-    out.codes = encode8<QD>(v);
+    if constexpr (POW2 && MODE == kApplyScaledCvt) {
+        out.codes = encode8_pow2<QD>(x, sc.s);
+    } else {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = scaled<QD, POW2, MODE>(x[i], sc.s, sc.inv);
+        out.codes = encode8<QD>(v);
+    }
     return out;
 }
 
@@ -207,10 +250,10 @@ __device__ __forceinline__ uint32_t pack_e8_word(uint32_t e8, int lane)
 
 // The same for a per-token group held by G/8 consecutive lanes: each lane
 // brings its own 8 values' |max| bits, reduced here over the group.
-template <int G, int QD, bool POW2>
+template <int G, int QD, bool POW2, int MODE>
 __device__ __forceinline__ Quantized quantize_segment(const float (&x)[8], uint32_t amax_bits)
 {
-    return quantize_values<QD, POW2>(x, group_max<G>(amax_bits));
+    return quantize_values<QD, POW2, MODE>(x, group_max<G>(amax_bits));
 }
 
 // Code values back to fp32 (exact) with the hardware decoders, times s.

@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kWave * kNormMaxWaves) void rmsnorm_kernel(NormPara
                     y[i] = (x[i] * r) * wf[i];
                     amax = max(amax, __float_as_uint(y[i]) & 0x7FFFFFFFu);
                 }
-                const Quantized qz = quantize_segment<G, QD, POW2>(y, amax);
+                const Quantized qz = quantize_segment<G, QD, POW2, kApplyScaledCvt>(y, amax);
                 if constexpr (QD == kE4M3) store8(qrow, col, qz.codes);
                 else store4(qrow, col / 2, qz.codes.x);
                 if constexpr (SF == kScaleF32) {
@@ -430,7 +430,7 @@ __device__ __forceinline__ Quantized norm_segment(const u32x4 &xk, float r, cons
         y[i] = (x[i] * r) * wf[i];
         amax = __builtin_fmaxf(amax, __builtin_fabsf(y[i]));
     }
-    return quantize_segment<G, QD, POW2>(y, __float_as_uint(amax));
+    return quantize_segment<G, QD, POW2, kApplyScaledCvt>(y, __float_as_uint(amax));
 }
 
 // The segment's group scales into the wave's LDS slice of scale words.

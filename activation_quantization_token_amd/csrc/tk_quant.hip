@@ -212,7 +212,7 @@ template <int G, int QD, bool POW2, int SF>
 __device__ __forceinline__ void cast_segment(const float (&x)[8], uint32_t amax_bits, int lane, uint32_t col,
                                              __amdgpu_buffer_rsrc_t qrow, __amdgpu_buffer_rsrc_t srow)
 {
-    store_segment<G, QD, SF>(quantize_segment<G, QD, POW2>(x, amax_bits), lane, col, qrow, srow);
+    store_segment<G, QD, SF>(quantize_segment<G, QD, POW2, kApplyClamp>(x, amax_bits), lane, col, qrow, srow);
 }
 
 // ---------------------------------------------------------------------------
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(1024) void cast_rows_kernel(CastParams p)
                 float x[8];
                 widen8(w[k], x);
                 const uint32_t amax = amax_bits_bf16x8(w[k]);
-                const Quantized qz = quantize_segment<G, QD, POW2>(x, amax);
+                const Quantized qz = quantize_segment<G, QD, POW2, kApplyClamp>(x, amax);
                 if constexpr (QD == kE4M3) store8(qrow, col, qz.codes);
                 else store4(qrow, col / 2, qz.codes.x);
                 if constexpr (SF == kScaleF32) {
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(1024) void cast_rows_f32_kernel(CastParams p)
                 const Scale<QD, POW2> sc = group_scale<QD, POW2>(piece_group_max<G>(amax, lane));
                 float v[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = scaled<QD, POW2>(__uint_as_float(w[k][i]), sc.s, sc.inv);
+                for (int i = 0; i < 4; ++i) v[i] = scaled<QD, POW2, kApplyClamp>(__uint_as_float(w[k][i]), sc.s, sc.inv);
                 const uint32_t codes = encode4<QD>(v);
                 if constexpr (QD == kE4M3) store4(qrow, col, codes);
                 else __builtin_amdgcn_raw_buffer_store_b16(uint16_t(codes), qrow, int(col / 2), 0, kNonTemporal);
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kWave * WPB) void cast_back_kernel(BackParams p)
         for (int k = 0; k < U; ++k) {
             float x[8], y[8];
             widen8(w[k], x);
-            const Quantized qz = quantize_segment<G, QD, POW2>(x, amax_bits_bf16x8(w[k]));
+            const Quantized qz = quantize_segment<G, QD, POW2, kApplyClamp>(x, amax_bits_bf16x8(w[k]));
             dequant_codes<QD>(qz.codes, qz.s, y);
             store16(yrow, (un.col0 + k * kSegCols) * 2u, pack_bf16x8(y));
         }
@@ -616,7 +616,7 @@ __global__ __launch_bounds__(kWave * WPB) void swiglu_cast_kernel(CastParams p)
                     amax = max(amax, __float_as_uint(h[i]) & 0x7FFFFFFFu);
                 }
             }
-            qz[k] = quantize_segment<G, QD, POW2>(h, amax);
+            qz[k] = quantize_segment<G, QD, POW2, kApplyMul>(h, amax);
             if constexpr (QD == kE4M3) store8(qrow, un.col0 + k * kSegCols, qz[k].codes);
             else store4(qrow, (un.col0 + k * kSegCols) / 2, qz[k].codes.x);
         }

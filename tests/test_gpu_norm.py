@@ -245,3 +245,16 @@ def test_rmsnorm_cast_equals_cast_of_rmsnorm_output():
     b = tk.rmsnorm_cast(x, wt, 1e-6, w.group, w.out_dtype, w.round_pow2, w.scale_fmt)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("dt,p2,sf", VARIANTS)
+@pytest.mark.parametrize("cols,group", [(7168, 32), (7168, 128), (2048, 16), (16384, 64)])
+def test_rmsnorm_cast_rounding_edges(dt, p2, sf, cols, group):
+    """Rows on which y equals chosen bf16 values exactly (tests/norm_edges.py):
+    every code value, every midpoint between codes, the subnormal codes,
+    signed zeros and values that round to zero, at group scales 2^-24 .. 2^1
+    and under the 1e-4 floor, through both RMSNorm kernels (one wave per row
+    up to 7168 channels, a workgroup per row above)."""
+    import norm_edges
+    x, w = norm_edges.edge_rows(cols, group, dt)
+    check_norm_cast(x, w, 1e-6, group, dt, p2, sf, label="rounding edges")

@@ -126,3 +126,24 @@ def test_rmsnorm_rejects_bad_arguments():
             oracle.rmsnorm(x, None, eps)
     with pytest.raises(ValueError):
         oracle.rmsnorm_cast(x, None, 1e-6, 48)
+
+
+@pytest.mark.parametrize("cols,group", [(7168, 32), (7168, 128), (2048, 16), (16384, 64)])
+@pytest.mark.parametrize("dt", ["e4m3", "e2m1"])
+def test_edge_rows_make_y_equal_x(cols, group, dt):
+    """The rounding-edge rows (tests/norm_edges.py) do what their construction
+    claims under the oracle: r = 2^-M exactly, so y equals x on every test
+    column and 16 on the anchors; every group leads with its maximum D * 2^k."""
+    import norm_edges
+    x, w = norm_edges.edge_rows(cols, group, dt, ks=[-24, -9, 0, 1])
+    y = oracle.rmsnorm(x, w, 1e-6, "f32")
+    mask = norm_edges.edge_columns(cols, group)
+    assert np.array_equal(y[:, mask].view(np.uint32), x[:, mask].astype(np.uint32) << 16)
+    tail = y[:, ~mask]
+    assert np.all((tail == 16.0) | (tail == 0.0)) and np.count_nonzero(tail == 16.0) == x.shape[0] * (cols // 256)
+    d = 448.0 if dt == "e4m3" else 6.0
+    lead = x[:, :int(mask.sum())].reshape(x.shape[0], -1, group)[:, :, 0]
+    assert set(np.unique(lead).tolist()) <= {int(bf16([d * 2.0 ** k])[0]) for k in (-24, -9, 0, 1)}
+    q, _ = oracle.rmsnorm_cast(x, w, 1e-6, group, dt, True, "f32")
+    codes = np.unique(q) if dt == "e4m3" else np.unique(np.concatenate([q & 0xF, q >> 4]))
+    assert codes.size == (254 if dt == "e4m3" else 16), "the rows do not reach every code"
