@@ -380,11 +380,23 @@ __device__ float exact_sum_squares_wave(const u32x4 (&xs)[NS], unsigned long lon
     return __uint_as_float(__builtin_amdgcn_readfirstlane(result));
 }
 
+// The weight row in LDS, fp32, split per 512-column segment into two halves:
+// weights col .. col+3 of the 8 that lane l of a segment holds (col = 512 k
+// + 8 l) sit at 512 k + 4 l, weights col+4 .. col+7 at 512 k + 256 + 4 l.
+// Each 16-byte read of a wave then covers 1 KiB of consecutive LDS; in
+// column order the lanes' reads lie 32 bytes apart and collide pairwise on
+// the banks (16.5 M conflict cycles per call at 32768 x 7168).
+__device__ __forceinline__ uint32_t weight_slot(uint32_t col)   // col a multiple of 8
+{
+    return (col & ~511u) + ((col & 511u) >> 1);
+}
+
 // 8 consecutive fp32 weights from LDS (col a multiple of 8: two 16-byte reads)
 __device__ __forceinline__ void weight8(const float *w, uint32_t col, float (&wf)[8])
 {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(w + col), b = *reinterpret_cast<const f32x4 *>(w + col + 4);
+    const uint32_t at = weight_slot(col);
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(w + at), b = *reinterpret_cast<const f32x4 *>(w + at + 256);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         wf[i] = a[i];
@@ -547,7 +559,8 @@ __global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void r
     if (row < p.rows) load_row(row);
 
     // Weight row into LDS as fp32 (w_j, or 1.0 without a weight; 0 past the
-    // row end), read in 16-byte pieces that are all in flight at once.
+    // row end) in the layout of weight_slot, read from memory in 16-byte
+    // pieces that are all in flight at once.
     {
         constexpr int kPieces = kCols / 8;                                  // 8 weights each
         constexpr int kPerThread = (kPieces + kWave * kNormWaveWPB - 1) / (kWave * kNormWaveWPB);
@@ -568,8 +581,9 @@ __global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void r
 #pragma unroll
                     for (int i = 0; i < 8; ++i) f[i] = piece * 8u + i < cols ? 1.0f : 0.0f;
                 }
-                *reinterpret_cast<f32x4 *>(lds_weight + piece * 8u) = f32x4{f[0], f[1], f[2], f[3]};
-                *reinterpret_cast<f32x4 *>(lds_weight + piece * 8u + 4u) = f32x4{f[4], f[5], f[6], f[7]};
+                const uint32_t at = weight_slot(piece * 8u);
+                *reinterpret_cast<f32x4 *>(lds_weight + at) = f32x4{f[0], f[1], f[2], f[3]};
+                *reinterpret_cast<f32x4 *>(lds_weight + at + 256u) = f32x4{f[4], f[5], f[6], f[7]};
             }
         }
     }

@@ -694,6 +694,7 @@ using KernelFn = void (*)(CastParams);
 constexpr int kCastU = TK_CAST_U, kCastWPB = TK_CAST_WPB;
 constexpr int kSwigluU = TK_SWIGLU_U, kSwigluWPB = TK_SWIGLU_WPB;
 constexpr int kSwigluBlocksPerCU = TK_SWIGLU_BLOCKS_PER_CU;
+constexpr int64_t kSwigluShortUnits = 1;
 
 #ifndef TK_CAST_ROWS
 #define TK_CAST_ROWS 1
@@ -739,33 +740,34 @@ struct KernelTable {
     KernelFn fn[4][2][3];
 };
 
-template <bool SWIGLU, int G, int QD, bool POW2, int SF>
+template <bool SWIGLU, int G, int QD, bool POW2, int SF, int SU>
 constexpr KernelFn pick()
 {
-    if constexpr (SWIGLU) return swiglu_cast_kernel<G, QD, POW2, SF, kSwigluU, kSwigluWPB>;
+    if constexpr (SWIGLU) return swiglu_cast_kernel<G, QD, POW2, SF, SU, kSwigluWPB>;
     else return cast_kernel<G, QD, POW2, SF, kCastU, kCastWPB>;
 }
 
-template <bool SWIGLU, int G, int QD>
+template <bool SWIGLU, int G, int QD, int SU>
 void fill_variants(KernelFn (&t)[3])
 {
-    t[0] = pick<SWIGLU, G, QD, false, kScaleF32>();
-    t[1] = pick<SWIGLU, G, QD, true, kScaleF32>();
-    t[2] = pick<SWIGLU, G, QD, true, kScaleUE8M0>();
+    t[0] = pick<SWIGLU, G, QD, false, kScaleF32, SU>();
+    t[1] = pick<SWIGLU, G, QD, true, kScaleF32, SU>();
+    t[2] = pick<SWIGLU, G, QD, true, kScaleUE8M0, SU>();
 }
 
-template <bool SWIGLU>
+// SU: segments per SwiGLU unit (the plain cast's unit form always takes kCastU).
+template <bool SWIGLU, int SU = kSwigluU>
 KernelTable make_table()
 {
     KernelTable t;
-    fill_variants<SWIGLU, 16, kE4M3>(t.fn[0][0]);
-    fill_variants<SWIGLU, 16, kE2M1>(t.fn[0][1]);
-    fill_variants<SWIGLU, 32, kE4M3>(t.fn[1][0]);
-    fill_variants<SWIGLU, 32, kE2M1>(t.fn[1][1]);
-    fill_variants<SWIGLU, 64, kE4M3>(t.fn[2][0]);
-    fill_variants<SWIGLU, 64, kE2M1>(t.fn[2][1]);
-    fill_variants<SWIGLU, 128, kE4M3>(t.fn[3][0]);
-    fill_variants<SWIGLU, 128, kE2M1>(t.fn[3][1]);
+    fill_variants<SWIGLU, 16, kE4M3, SU>(t.fn[0][0]);
+    fill_variants<SWIGLU, 16, kE2M1, SU>(t.fn[0][1]);
+    fill_variants<SWIGLU, 32, kE4M3, SU>(t.fn[1][0]);
+    fill_variants<SWIGLU, 32, kE2M1, SU>(t.fn[1][1]);
+    fill_variants<SWIGLU, 64, kE4M3, SU>(t.fn[2][0]);
+    fill_variants<SWIGLU, 64, kE2M1, SU>(t.fn[2][1]);
+    fill_variants<SWIGLU, 128, kE4M3, SU>(t.fn[3][0]);
+    fill_variants<SWIGLU, 128, kE2M1, SU>(t.fn[3][1]);
     return t;
 }
 
@@ -790,6 +792,7 @@ tk_status launch(bool swiglu, const void *x, int64_t rows, int64_t cols, int64_t
 
     static const KernelTable cast_table = make_table<false>();
     static const KernelTable swiglu_table = make_table<true>();
+    static const KernelTable swiglu_short_table = make_table<true, 1>();
     const int variant = !round_pow2 ? 0 : (scale_fmt == kScaleF32 ? 1 : 2);
     const int64_t s_words = scale_fmt == kScaleF32 ? cols / group : cols / group / 4;
     if (!swiglu && kCastRows && s_words * 4 <= kRowScaleLdsBytes) {
@@ -806,10 +809,18 @@ tk_status launch(bool swiglu, const void *x, int64_t rows, int64_t cols, int64_t
             return TK_ERROR_LAUNCH;
         return TK_SUCCESS;
     }
-    const KernelFn fn = (swiglu ? swiglu_table : cast_table).fn[group_index(group)][out_dtype][variant];
-    const int U = swiglu ? kSwigluU : kCastU;
-    const int wpb = swiglu ? kSwigluWPB : kCastWPB;
+    // SwiGLU: one-segment units while the persistent grid has a wave for each
+    // of them, kSwigluU segments per unit above.  Measured on MI355X at 2048
+    // columns: one-segment units 11 % faster at 2048 rows (one unit per
+    // wave); two-segment units 2.8 % faster at 8192 rows on the workload's
+    // gate N(0, std 2) and up N(0, 1) (four units per wave) and 4 % at 32768.
     const int64_t nseg = (cols + kSegCols - 1) / kSegCols;
+    const bool short_units =
+        swiglu && rows * nseg <= int64_t(info->cus) * kSwigluBlocksPerCU * kSwigluWPB * kSwigluShortUnits;
+    const KernelTable &table = !swiglu ? cast_table : short_units ? swiglu_short_table : swiglu_table;
+    const KernelFn fn = table.fn[group_index(group)][out_dtype][variant];
+    const int U = !swiglu ? kCastU : short_units ? 1 : kSwigluU;
+    const int wpb = swiglu ? kSwigluWPB : kCastWPB;
     const int64_t units = rows * ((nseg + U - 1) / U);
     int64_t blocks = (units + wpb - 1) / wpb;
     const int64_t cap = swiglu ? int64_t(info->cus) * kSwigluBlocksPerCU : int64_t(0x7FFFFFFF);

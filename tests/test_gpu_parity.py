@@ -168,6 +168,21 @@ def test_swiglu_sweep(group, dt, p2, sf, rows, cols):
     check(gate_up, group, dt, p2, sf, swiglu=True, x_ld=2 * cols + 16, label="swiglu-sweep")
 
 
+@pytest.mark.parametrize("rows,cols,group,dt,p2,sf", [(2048, 2048, 128, "e4m3", True, "f32"),
+                                                     (585, 7168, 32, "e2m1", True, "ue8m0"),
+                                                     (2049, 2048, 128, "e4m3", True, "f32"),
+                                                     (9000, 2048, 32, "e2m1", True, "ue8m0"),
+                                                     (3000, 7168, 64, "e4m3", False, "f32")])
+def test_swiglu_unit_sizes(rows, cols, group, dt, p2, sf):
+    """Both SwiGLU unit sizes: one-segment units while rows x segments is at
+    most the persistent grid's wave count (8192 on 256 CUs: 2048 x 2048 and
+    585 x 7168 are such shapes), two-segment units above (2049 x 2048 and
+    beyond)."""
+    gate = inputs.generate_small(rows + cols + group, rows, cols)
+    up = inputs.generate_small(rows + cols + group + 1, rows, cols, "student_t3")
+    check(np.concatenate([gate, up], axis=1), group, dt, p2, sf, swiglu=True, label="swiglu-units")
+
+
 def test_swiglu_every_gate_pattern():
     """Every finite bf16 gate appears once; the up value is 0.5 next to gates
     beyond 2^100 so that h stays finite."""
