@@ -183,6 +183,22 @@ def test_swiglu_unit_sizes(rows, cols, group, dt, p2, sf):
     check(np.concatenate([gate, up], axis=1), group, dt, p2, sf, swiglu=True, label="swiglu-units")
 
 
+@pytest.mark.parametrize("rows,cols,group,dt,p2,sf", [(4096, 7168, 128, "e4m3", True, "f32"),
+                                                     (3000, 9728, 32, "e2m1", True, "ue8m0"),
+                                                     (410, 40960, 16, "e2m1", True, "ue8m0"),
+                                                     (4097, 7168, 128, "e4m3", True, "f32"),
+                                                     (1000, 30720, 64, "e4m3", False, "f32"),
+                                                     (2047, 7168, 32, "e4m3", True, "ue8m0")])
+def test_cast_run_lengths(rows, cols, group, dt, p2, sf):
+    """Both run lengths of the row-form cast.  4-segment runs for inputs of up
+    to 4096 x 7168 values whose grid fills the chip's 32 x 256 wave slots (the
+    first three shapes: at the boundary, a ragged last run, more runs than
+    waves); 2-segment runs above that size and below that grid (the last
+    three: 2047 rows of 4 runs are one wave short)."""
+    x = inputs.generate_small(rows + cols + group, rows, cols, "student_t3" if rows % 2 else "normal")
+    check(x, group, dt, p2, sf, label="run-lengths")
+
+
 def test_swiglu_every_gate_pattern():
     """Every finite bf16 gate appears once; the up value is 0.5 next to gates
     beyond 2^100 so that h stays finite."""
