@@ -126,6 +126,7 @@ __global__ __launch_bounds__(kWave * kMaxBlockWaves) void block_cast_kernel(Bloc
 #endif
 constexpr int kChannelWPB = TK_CHANNEL_WPB;        // waves per workgroup
 constexpr int kChannelUnroll = TK_CHANNEL_UNROLL;  // rows in flight per wave
+constexpr int kChannelSmallUnroll = 2;             // the same for x of at most kChannelSmallBytes
 #ifndef TK_CHANNEL_REVERSE
 #define TK_CHANNEL_REVERSE 0
 #endif
@@ -138,6 +139,7 @@ constexpr bool kChannelReverse = TK_CHANNEL_REVERSE != 0;
 constexpr int kChannelFirstPassPolicy = TK_CHANNEL_P1_POLICY;
 constexpr int64_t kChannelMinChunkRows = 64;
 constexpr int64_t kChannelCachedBytes = int64_t(128) << 20;   // half the 256 MiB Infinity Cache
+constexpr int64_t kChannelSmallBytes = int64_t(64) << 20;
 constexpr int64_t kChannelMaxChunks = 32;
 static_assert(kChannelMaxChunks % kChannelWPB == 0, "each wave reduces the same number of chunks");
 
@@ -209,6 +211,7 @@ __device__ __forceinline__ void workgroup_max(u16x2 (&mx)[4], u32x4 (&part)[kCha
 }
 
 // Pass 1: the |max| of each column over one chunk of rows.
+template <int U>
 __global__ __launch_bounds__(kWave * kChannelWPB) void channel_amax_kernel(ChannelParams p)
 {
     __shared__ u32x4 part[kChannelWPB][kWave];
@@ -221,22 +224,22 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_amax_kernel(Chann
     const int64_t c0 = chunk * p.chunk_rows;
     const int64_t c1 = c0 + p.chunk_rows < p.rows ? c0 + p.chunk_rows : p.rows;
     const uint32_t col = stripe * uint32_t(kSegCols) + uint32_t(lane) * 8u;
-    const RowBatches<kChannelUnroll, kChannelFirstPassPolicy> rb{p.x, p.x_ld, c0, c1, cols * 2u, col * 2u, wave};
+    const RowBatches<U, kChannelFirstPassPolicy> rb{p.x, p.x_ld, c0, c1, cols * 2u, col * 2u, wave};
     // Running maxima of |x| as bf16 magnitudes, two per word (unsigned
     // 16-bit order is numeric order for them).
     u16x2 mx[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) mx[j] = u16x2{0, 0};
     const int64_t nb = rb.batches();
-    u32x4 w[kChannelUnroll];
+    u32x4 w[U];
     rb.load(0, w);
     for (int64_t b = 0; b < nb; ++b) {
-        u32x4 wn[kChannelUnroll];
+        u32x4 wn[U];
         rb.load(b + 1, wn);                 // all-zero past the chunk's end
 #pragma unroll
-        for (int k = 0; k < kChannelUnroll; ++k) max_bf16x8(mx, w[k]);
+        for (int k = 0; k < U; ++k) max_bf16x8(mx, w[k]);
 #pragma unroll
-        for (int k = 0; k < kChannelUnroll; ++k) w[k] = wn[k];
+        for (int k = 0; k < U; ++k) w[k] = wn[k];
     }
     workgroup_max(mx, part, wave, lane);
     if (wave == 0) {
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_amax_kernel(Chann
 // are reduced, so their latencies overlap.  P2_POLICY: the loads' cache
 // policy (ordinary when x is small enough to stay in the Infinity Cache,
 // where the first pass left it; non-temporal otherwise).
-template <int QD, bool POW2, int SF, int P2_POLICY>
+template <int QD, bool POW2, int SF, int P2_POLICY, int U>
 __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(ChannelParams p)
 {
     __shared__ u32x4 part[kChannelWPB][kWave];
@@ -265,12 +268,12 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(Chann
     const int64_t c0 = chunk * p.chunk_rows;
     const int64_t c1 = c0 + p.chunk_rows < p.rows ? c0 + p.chunk_rows : p.rows;
     const uint32_t col = stripe * uint32_t(kSegCols) + uint32_t(lane) * 8u;
-    const RowBatches<kChannelUnroll, P2_POLICY> rb{p.x, p.x_ld, c0, c1, cols * 2u, col * 2u, wave};
+    const RowBatches<U, P2_POLICY> rb{p.x, p.x_ld, c0, c1, cols * 2u, col * 2u, wave};
     const int64_t nb = rb.batches();
     // Batch order: descending when kChannelReverse, so that the rows the
     // first pass read last (the likeliest still cached) come first.
     auto batch_at = [&](int64_t i) { return kChannelReverse ? nb - 1 - i : i; };
-    u32x4 w[kChannelUnroll];
+    u32x4 w[U];
     rb.load(batch_at(0), w);
 
     // Column maxima of this lane's 8 columns over every chunk: wave w takes
@@ -321,10 +324,10 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(Chann
 
     const uint32_t qbytes = QD == kE4M3 ? cols : cols / 2;
     for (int64_t i = 0; i < nb; ++i) {
-        u32x4 wn[kChannelUnroll];
+        u32x4 wn[U];
         rb.load(batch_at(i + 1), wn);       // nothing past the last batch
 #pragma unroll
-        for (int k = 0; k < kChannelUnroll; ++k) {
+        for (int k = 0; k < U; ++k) {
             const int64_t row = rb.row(batch_at(i), k);
             if (row < c1) {
                 float x[8], v[8];
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(Chann
             }
         }
 #pragma unroll
-        for (int k = 0; k < kChannelUnroll; ++k) w[k] = wn[k];
+        for (int k = 0; k < U; ++k) w[k] = wn[k];
     }
 }
 
@@ -352,7 +355,7 @@ struct BlockTable {
     BlockFn fn[3][4][2][3];      // [rows per wave 4/8/16][block_cols index][code format][variant]
 };
 struct ChannelTable {
-    ChannelFn cast[2][3][2];     // [code format][variant][second-pass loads: non-temporal, ordinary]
+    ChannelFn cast[2][3][3];     // [code format][variant][x above 128 MiB, up to 128 MiB, up to 64 MiB]
 };
 
 template <int BC, int QD, int RPW>
@@ -395,9 +398,10 @@ int block_rpw_index(int64_t block_rows, int64_t tiles, int cus)
 template <int QD, int PI, int POL>
 void fill_channel_policy(ChannelTable &t)
 {
-    t.cast[QD][0][PI] = channel_cast_kernel<QD, false, kScaleF32, POL>;
-    t.cast[QD][1][PI] = channel_cast_kernel<QD, true, kScaleF32, POL>;
-    t.cast[QD][2][PI] = channel_cast_kernel<QD, true, kScaleUE8M0, POL>;
+    constexpr int U = PI == 2 ? kChannelSmallUnroll : kChannelUnroll;
+    t.cast[QD][0][PI] = channel_cast_kernel<QD, false, kScaleF32, POL, U>;
+    t.cast[QD][1][PI] = channel_cast_kernel<QD, true, kScaleF32, POL, U>;
+    t.cast[QD][2][PI] = channel_cast_kernel<QD, true, kScaleUE8M0, POL, U>;
 }
 
 template <int QD>
@@ -405,6 +409,7 @@ void fill_channel(ChannelTable &t)
 {
     fill_channel_policy<QD, 0, kNonTemporal>(t);
     fill_channel_policy<QD, 1, 0>(t);
+    fill_channel_policy<QD, 2, 0>(t);
 }
 
 ChannelTable make_channel_table()
@@ -525,14 +530,18 @@ tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t
     ChannelParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld, scales,
                     static_cast<uint16_t *>(workspace), chunk_rows, chunks};
     void *args[] = {&p};
-    if (hipLaunchKernel(reinterpret_cast<const void *>(channel_amax_kernel), dim3(uint32_t(tiles)),
-                        dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
-        return TK_ERROR_LAUNCH;
-    // Second pass: ordinary loads while x takes at most half the 256 MiB
-    // Infinity Cache (measured with inputs rotated over three buffer sets:
+    // Size classes of x.  Up to half the 256 MiB Infinity Cache the second
+    // pass uses ordinary loads (with inputs rotated over three buffer sets:
     // -6 % at 4096 x 7168; at 16384 x 7168, 235 MB, ordinary loads were 4 %
-    // slower), non-temporal beyond.
-    const int pi = rows * cols * 2 <= kChannelCachedBytes ? 1 : 0;
+    // slower), non-temporal ones beyond; up to 64 MiB both passes keep 2 rows
+    // in flight per wave instead of 4 (-10 % at 4096 x 7168; 1 % slower at
+    // 8192 rows, 2-5 % at 16384 and 32768).
+    const int64_t x_bytes = rows * cols * 2;
+    const int pi = x_bytes <= kChannelSmallBytes ? 2 : x_bytes <= kChannelCachedBytes ? 1 : 0;
+    const void *amax_fn = pi == 2 ? reinterpret_cast<const void *>(channel_amax_kernel<kChannelSmallUnroll>)
+                                  : reinterpret_cast<const void *>(channel_amax_kernel<kChannelUnroll>);
+    if (hipLaunchKernel(amax_fn, dim3(uint32_t(tiles)), dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
+        return TK_ERROR_LAUNCH;
     if (hipLaunchKernel(reinterpret_cast<const void *>(table.cast[out_dtype][variant][pi]), dim3(uint32_t(tiles)),
                         dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
         return TK_ERROR_LAUNCH;

@@ -155,6 +155,16 @@ def test_per_channel_full_size(dt, p2, sf, w):
     check_channel(x, dt, p2, sf, label="full size")
 
 
+@pytest.mark.parametrize("rows", [4681, 4682, 9362, 9363])
+def test_per_channel_size_classes(rows):
+    """Both sides of the per-channel cast's size boundaries at 7168 columns:
+    x of at most 64 MiB (4681 rows; 2 rows in flight per wave), at most
+    128 MiB (4682 and 9362 rows; ordinary second-pass loads), and above
+    (9363 rows; non-temporal)."""
+    x = inputs.generate_small(rows, rows, 7168, "student_t3")
+    check_channel(x, "e4m3", True, "ue8m0", label="size classes")
+
+
 def test_per_channel_zero_columns_and_reused_workspace():
     """Columns of zeros take the floored scale; one workspace serves a larger
     and then a smaller call (its contents on entry do not matter)."""
