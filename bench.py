@@ -66,7 +66,7 @@ def _pmc_per_kernel(csv_path, counter):
     return {k: list(v.values()) for k, v in vals.items()}
 
 
-def summarize_pmc(workload_index, fetch_csv, write_csv):
+def summarize_pmc(workload_index, fetch_csv, write_csv, traffic_file=None):
     """HBM bytes per cast launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for the library's 1 GiB
     streaming copy in the same run (known size: 1 GiB read, 1 GiB written)."""
@@ -92,14 +92,16 @@ def summarize_pmc(workload_index, fetch_csv, write_csv):
         "algorithmic_bytes_per_launch": w.algorithmic_bytes(),
         "ratio_to_algorithmic": round(hbm / w.algorithmic_bytes(), 5),
     }
+    out = pathlib.Path(traffic_file) if traffic_file is not None else TRAFFIC_FILE
     try:
-        data = json.loads(TRAFFIC_FILE.read_text())
+        data = json.loads(out.read_text())
     except (OSError, ValueError):
         data = {}
     data[f"workload{workload_index}"] = entry
-    TRAFFIC_FILE.parent.mkdir(exist_ok=True)
-    TRAFFIC_FILE.write_text(json.dumps(data, indent=2) + "\n")
+    out.parent.mkdir(exist_ok=True)
+    out.write_text(json.dumps(data, indent=2) + "\n")
     print(json.dumps(entry, indent=2))
+    return entry
 
 
 def _oracle_step(op: str, w, block, weight_bits):
