@@ -61,6 +61,26 @@ __device__ __forceinline__ void store_scale(__amdgpu_buffer_rsrc_t r, uint32_t b
 }
 
 // ---------------------------------------------------------------------------
+// Workgroup order across the XCDs.  A launch's workgroups go to the MI355X's
+// 8 XCDs round robin (workgroup b to XCD b % 8), and each XCD has its own L2.
+// xcd_order renumbers the workgroups of a grid that takes n items once each
+// so that every XCD gets runs of 2^L consecutive items: in each group of
+// 8 * 2^L items, workgroup b takes item (b % 8) * 2^L + (b % (8 * 2^L)) / 8
+// of the group.  The items of a last, partial group keep their own index,
+// and L < 0 leaves every index alone, so this is a bijection on [0, n).
+// The resident workgroups still cover one compact window of the tensor, but
+// each XCD's share of it is contiguous instead of every eighth item.
+
+__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t n, int L)
+{
+    if (L < 0) return b;
+    const int64_t group = int64_t(8) << L;
+    if (b >= n - (n & (group - 1))) return b;
+    const int64_t in = b & (group - 1);
+    return (b - in) + ((in & 7) << L) + (in >> 3);
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane helpers.
 
 template <int CTRL>

@@ -28,16 +28,18 @@ __global__ __launch_bounds__(kCopyBlock) void copy_stream_kernel(const u32x4 *sr
 // the wave read, so no load can be dropped.  Of the plain streams measured on
 // MI355X at the cast's 4:1 and 2:1 read:write volumes (grid-stride loops of
 // 2-8 KiB per wave step, one-shot waves of 1, 2 or 4 KiB, 4, 7 or 16 waves
-// per workgroup), this shape was the fastest.
+// per workgroup), this shape was the fastest; its workgroups take the
+// row-form cast's XCD order (xcd_order).
 constexpr int kStreamWaves = 7;
 constexpr int64_t kStreamWaveBytes = 2048;
 
 __global__ __launch_bounds__(kWave * kStreamWaves) void stream_rw_kernel(const uint8_t *src, int64_t read_bytes,
                                                                        uint8_t *dst, int64_t write_bytes,
-                                                                       int64_t wpw)
+                                                                       int64_t wpw, int xcd_log2)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = int64_t(blockIdx.x) * kStreamWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wave = xcd_order(blockIdx.x, gridDim.x, xcd_log2) * kStreamWaves +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t r0 = wave * kStreamWaveBytes, w0 = wave * wpw;
     const int64_t rn = read_bytes - r0, wn = write_bytes - w0;
     const __amdgpu_buffer_rsrc_t r =
@@ -100,7 +102,9 @@ tk_status tk_stream_rw(const void *src, int64_t read_bytes, void *dst, int64_t w
     const uint8_t *sp = static_cast<const uint8_t *>(src);
     uint8_t *dp = static_cast<uint8_t *>(dst);
     int64_t rb = read_bytes, wb = write_bytes;
-    void *args[] = {&sp, &rb, &dp, &wb, &wpw};
+    // workgroups in the row-form cast's XCD order (14 KiB read each)
+    int xl = xcd_run_log2(blocks, blocks, kStreamWaves * kStreamWaveBytes);
+    void *args[] = {&sp, &rb, &dp, &wb, &wpw, &xl};
     if (hipLaunchKernel(reinterpret_cast<const void *>(stream_rw_kernel), dim3(uint32_t(blocks)),
                         dim3(kWave * kStreamWaves), args, 0, static_cast<hipStream_t>(stream)) != hipSuccess)
         return TK_ERROR_LAUNCH;

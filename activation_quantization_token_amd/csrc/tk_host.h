@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "tk_quant.h"
@@ -18,8 +19,11 @@ struct DeviceInfo {
     std::once_flag once;
     tk_status status = TK_ERROR_DEVICE;
     int cus = 0;
-    std::once_flag table_once;
-    tk_status table_status = TK_ERROR_DEVICE;
+    // The SwiGLU form's silu32 table: built under table_mutex, table_ready
+    // set only once the build has finished on the device, so that a failed
+    // build is tried again by the next call.
+    std::mutex table_mutex;
+    std::atomic<bool> table_ready{false};
 };
 DeviceInfo g_devices[kMaxDevices];
 
@@ -41,5 +45,34 @@ tk_status device_info(int *dev_out, DeviceInfo **info_out)
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Run length (log2 of items) of xcd_order for a grid of `grid` workgroups
+// over n items, each workgroup reading item_bytes of input: runs of about
+// 1 MiB of input per XCD, 512 KiB when the whole input is at most 56 MiB
+// (4096 x 7168 bf16), and -1 (no renumbering) when the grid loops over the
+// items.  Measured on MI355X with the row-form cast at 7168 channels (one
+// 14 KiB row per workgroup): runs of 64 rows 2.9 % faster than every-eighth-
+// row order at 32768 rows and 2.4 % at 16384, runs of 32 rows 2 % at 4096;
+// runs of 256 rows and more, and one contiguous eighth per XCD, were slower
+// than no renumbering at all.
+#ifndef TK_XCD_RUN_SHIFT
+#define TK_XCD_RUN_SHIFT 0
+#endif
+constexpr int64_t kXcdRunBytes = int64_t(1) << 20;
+constexpr int64_t kXcdSmallRunBytes = int64_t(1) << 19;
+constexpr int64_t kXcdSmallInputBytes = int64_t(4096) * 7168 * 2;
+
+inline int xcd_run_log2(int64_t n, int64_t grid, int64_t item_bytes)
+{
+#ifdef TK_XCD_OFF
+    return -1;
+#endif
+    if (grid != n || item_bytes <= 0) return -1;
+    const int64_t target = n * item_bytes <= kXcdSmallInputBytes ? kXcdSmallRunBytes : kXcdRunBytes;
+    int L = 0;
+    while (L < 12 && (item_bytes << (L + 1)) <= target) ++L;
+    L += TK_XCD_RUN_SHIFT;
+    return L < 0 ? 0 : L;
+}
 
 }  // namespace

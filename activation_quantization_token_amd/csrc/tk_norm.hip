@@ -1,6 +1,7 @@
 // tk_norm.hip -- gfx950 kernels and C ABI for RMSNorm forward, alone and
 // with the per-token cast fused after it ("TileKernels" (aiwiki.ai), Version
-// 2.0.0: RMSNorm forward with an optional fused FP8 cast).  The arithmetic
+// 2.0.0: RMSNorm forward, which can be followed by an FP8 cast in the same
+// kernel).  The arithmetic
 // contract is written out in include/tk_quant.h.
 //
 // Design.  Rows of up to 7168 channels run one row per wave

@@ -45,6 +45,7 @@ struct CastParams {
     int64_t q_ld;
     void *s;
     int64_t s_ld;
+    int32_t xcd_log2;    // xcd_order run length of the row kernels (-1: none)
 };
 
 // ---------------------------------------------------------------------------
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(1024) void cast_rows_kernel(CastParams p)
     const int runs = int((cols + U * kSegCols - 1) / (U * kSegCols));
     const uint32_t s_words = SF == kScaleF32 ? cols / G : cols / G / 4;
     constexpr int kLanesPerGroup = G / 8;
-    for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
+    for (int64_t row = xcd_order(blockIdx.x, p.rows, p.xcd_log2); row < p.rows; row += gridDim.x) {
         const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + row * p.x_ld, cols * 2u);
         __amdgpu_buffer_rsrc_t qrow, srow;
         output_rows<G, QD, SF>(p, row, qrow, srow);
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(1024) void cast_rows_f32_kernel(CastParams p)
     const uint32_t s_words = SF == kScaleF32 ? cols / G : cols / G / 4;
     constexpr int kLanesPerGroup = G / 4;
     const float *xf = reinterpret_cast<const float *>(p.x);
-    for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
+    for (int64_t row = xcd_order(blockIdx.x, p.rows, p.xcd_log2); row < p.rows; row += gridDim.x) {
         const __amdgpu_buffer_rsrc_t xrow = row_buffer(xf + row * p.x_ld, cols * 4u);
         __amdgpu_buffer_rsrc_t qrow, srow;
         output_rows<G, QD, SF>(p, row, qrow, srow);
@@ -428,13 +429,15 @@ struct BackParams {
     int64_t rows, cols, x_ld;
     uint16_t *y;         // bf16 bits
     int64_t y_ld;
+    int32_t xcd_log2;    // xcd_order run length over the workgroups (-1: none)
 };
 
 template <int G, int QD, bool POW2, int U, int WPB>
 __global__ __launch_bounds__(kWave * WPB) void cast_back_kernel(BackParams p)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = int64_t(blockIdx.x) * WPB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wave = xcd_order(blockIdx.x, gridDim.x, p.xcd_log2) * WPB +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = int64_t(gridDim.x) * WPB;
     const int64_t nseg = (p.cols + kSegCols - 1) / kSegCols;
     const int64_t runs = (nseg + U - 1) / U;
@@ -466,13 +469,15 @@ struct DequantParams {
     int64_t s_ld;
     void *y;
     int64_t y_ld;        // elements of y's type
+    int32_t xcd_log2;    // xcd_order run length over the workgroups (-1: none)
 };
 
 template <int G, int QD, int SF, bool OUT_F32, int U, int WPB>
 __global__ __launch_bounds__(kWave * WPB) void dequant_kernel(DequantParams p)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = int64_t(blockIdx.x) * WPB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wave = xcd_order(blockIdx.x, gridDim.x, p.xcd_log2) * WPB +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = int64_t(gridDim.x) * WPB;
     const int64_t nseg = (p.cols + kSegCols - 1) / kSegCols;
     const int64_t runs = (nseg + U - 1) / U;
@@ -632,17 +637,25 @@ __global__ __launch_bounds__(kWave * WPB) void swiglu_cast_kernel(CastParams p)
 // ---------------------------------------------------------------------------
 // Host side.
 
+// Builds the current device's silu32 table once: a kernel on `stream`, then a
+// wait for it.  The launch's own return code is checked (not hipGetLastError,
+// which may hold an error left by an unrelated earlier call).  Inside a graph
+// capture the kernel would only be recorded, so the build is refused there.
 tk_status prepare_tables(DeviceInfo &d, hipStream_t stream)
 {
-    std::call_once(d.table_once, [&] {
-        const int threads = 256;
-        hipLaunchKernelGGL(silu_table_kernel, dim3((kSiluEntries + threads - 1) / threads), dim3(threads),
-                           0, stream);
-        if (hipGetLastError() != hipSuccess) { d.table_status = TK_ERROR_LAUNCH; return; }
-        if (hipStreamSynchronize(stream) != hipSuccess) { d.table_status = TK_ERROR_DEVICE; return; }
-        d.table_status = TK_SUCCESS;
-    });
-    return d.table_status;
+    if (d.table_ready.load(std::memory_order_acquire)) return TK_SUCCESS;
+    std::lock_guard<std::mutex> lock(d.table_mutex);
+    if (d.table_ready.load(std::memory_order_relaxed)) return TK_SUCCESS;
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &capture) != hipSuccess) return TK_ERROR_LAUNCH;
+    if (capture != hipStreamCaptureStatusNone) return TK_ERROR_UNSUPPORTED;
+    const int threads = 256;
+    if (hipLaunchKernel(reinterpret_cast<const void *>(silu_table_kernel),
+                        dim3((kSiluEntries + threads - 1) / threads), dim3(threads), nullptr, 0, stream) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    if (hipStreamSynchronize(stream) != hipSuccess) return TK_ERROR_DEVICE;
+    d.table_ready.store(true, std::memory_order_release);
+    return TK_SUCCESS;
 }
 
 tk_status validate(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void *q, int64_t q_ld,
@@ -813,7 +826,7 @@ tk_status launch(bool swiglu, const void *x, int64_t rows, int64_t cols, int64_t
         const int waves = int(runs < kRowMaxWaves ? runs : kRowMaxWaves);
         int64_t blocks = rows < int64_t(0x7FFFFFFF) ? rows : int64_t(0x7FFFFFFF);
         CastParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld,
-                     scales, s_ld};
+                     scales, s_ld, xcd_run_log2(rows, blocks, cols * 2)};
         void *args[] = {&p};
         const CastFn fn = (few ? row_table_few : row_table).fn[group_index(group)][out_dtype][variant];
         if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * waves), args,
@@ -838,7 +851,7 @@ tk_status launch(bool swiglu, const void *x, int64_t rows, int64_t cols, int64_t
     const int64_t cap = swiglu ? int64_t(info->cus) * kSwigluBlocksPerCU : int64_t(0x7FFFFFFF);
     if (blocks > cap) blocks = cap;     // the kernels loop over the remaining units
     CastParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld,
-                 scales, s_ld};
+                 scales, s_ld, -1};
     void *args[] = {&p};
     if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * wpb), args,
                         0, s) != hipSuccess)
@@ -895,12 +908,17 @@ DequantTable make_dequant_table()
 
 bool valid_group(int32_t g) { return g == 16 || g == 32 || g == 64 || g == 128; }
 
-tk_status launch_unit_grid(const void *fn, int64_t rows, int64_t cols, void *params, hipStream_t s)
+// params points to the kernel's parameter struct, xcd_log2 to its run-length
+// field; wg_bytes: the bytes one workgroup's units read or write, whichever
+// is more.
+tk_status launch_unit_grid(const void *fn, int64_t rows, int64_t cols, void *params, int32_t &xcd_log2,
+                           int64_t wg_bytes, hipStream_t s)
 {
     const int64_t nseg = (cols + kSegCols - 1) / kSegCols;
     const int64_t units = rows * ((nseg + kCastU - 1) / kCastU);
-    int64_t blocks = (units + kCastWPB - 1) / kCastWPB;
-    if (blocks > int64_t(0x7FFFFFFF)) blocks = 0x7FFFFFFF;   // the kernels loop over the rest
+    const int64_t need = (units + kCastWPB - 1) / kCastWPB;
+    const int64_t blocks = need > int64_t(0x7FFFFFFF) ? int64_t(0x7FFFFFFF) : need;   // the kernels loop
+    xcd_log2 = xcd_run_log2(need, blocks, wg_bytes);
     void *args[] = {params};
     if (hipLaunchKernel(fn, dim3(uint32_t(blocks)), dim3(kWave * kCastWPB), args, 0, s) != hipSuccess)
         return TK_ERROR_LAUNCH;
@@ -959,7 +977,7 @@ tk_status tk_per_token_cast_f32(const void *x, int64_t rows, int64_t cols, int64
     const int waves = int(runs < kRowMaxWaves ? runs : kRowMaxWaves);
     const int64_t blocks = rows < int64_t(0x7FFFFFFF) ? rows : int64_t(0x7FFFFFFF);
     CastParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld, scales,
-                 s_ld};
+                 s_ld, xcd_run_log2(rows, blocks, cols * 4)};
     void *args[] = {&p};
     const CastFn fn = table.fn[group_index(group)][out_dtype][variant];
     if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * waves), args,
@@ -984,9 +1002,10 @@ tk_status tk_per_token_cast_back(const void *x, int64_t rows, int64_t cols, int6
     tk_status st = device_info(&dev, &info);
     if (st != TK_SUCCESS) return st;
     static const BackTable table = make_back_table();
-    BackParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint16_t *>(y), y_ld};
+    BackParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint16_t *>(y), y_ld, -1};
     return launch_unit_grid(reinterpret_cast<const void *>(table.fn[group_index(group)][out_dtype][round_pow2 ? 1 : 0]),
-                            rows, cols, &p, static_cast<hipStream_t>(stream));
+                            rows, cols, &p, p.xcd_log2, int64_t(kCastWPB) * kCastU * kSegCols * 2,
+                            static_cast<hipStream_t>(stream));
 }
 
 tk_status tk_per_token_dequant(const void *q, int64_t rows, int64_t cols, int64_t q_ld, const void *scales,
@@ -1015,9 +1034,10 @@ tk_status tk_per_token_dequant(const void *q, int64_t rows, int64_t cols, int64_
     tk_status st = device_info(&dev, &info);
     if (st != TK_SUCCESS) return st;
     static const DequantTable table = make_dequant_table();
-    DequantParams p{static_cast<const uint8_t *>(q), rows, cols, q_ld, scales, s_ld, y, y_ld};
+    DequantParams p{static_cast<const uint8_t *>(q), rows, cols, q_ld, scales, s_ld, y, y_ld, -1};
     const DequantFn fn = table.fn[group_index(group)][in_dtype][scale_fmt][y_dtype == TK_OUT_F32 ? 1 : 0];
-    return launch_unit_grid(reinterpret_cast<const void *>(fn), rows, cols, &p, static_cast<hipStream_t>(stream));
+    return launch_unit_grid(reinterpret_cast<const void *>(fn), rows, cols, &p, p.xcd_log2,
+                            int64_t(kCastWPB) * kCastU * kSegCols * ysize, static_cast<hipStream_t>(stream));
 }
 
 tk_status tk_silu32_bf16(const void *g, void *out, int64_t n, void *stream)

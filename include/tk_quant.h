@@ -3,11 +3,12 @@
  * cast and its fused SwiGLU form.
  *
  * The operation (sources on the pages):
- *   - "Tile Kernels" (PyPI project page, v2.0.0), Features: per-token FP8 /
- *     FP4 casting of activations, and fused SwiGLU + quantization.
- *   - "TileKernels" (aiwiki.ai), section Quantization: the per-token cast takes
- *     BF16 activations, uses scale-factor groups of 16, 32, 64 or 128 channels,
- *     and can round scale factors to powers of two and pack them as UE8M0.
+ *   - "Tile Kernels" (PyPI project page, v2.0.0), Features: activations are
+ *     cast per token to FP8 or FP4, and SwiGLU has a form fused with the cast.
+ *   - "TileKernels" (aiwiki.ai), section Quantization: the per-token cast reads
+ *     BF16, gives each group of G channels of a row its own scale (G one of
+ *     16, 32, 64, 128), and can round scales up to powers of two and store
+ *     them packed as UE8M0 bytes.
  *   - "TileKernels, TileLang kernels for MoE routing and low-precision
  *     quantization" (hysenlabs.com), section "Seven kernel families": the
  *     SwiGLU and the narrowing run in one pass, with no intermediate tensor
@@ -37,8 +38,9 @@
  * stream) and return without waiting; outputs are valid once the stream
  * reaches that point.  The library allocates no per-call memory.  All
  * argument checks run on the host before anything is enqueued: on error
- * nothing is launched and the outputs are untouched.  Inputs with NaN or Inf
- * give unspecified codes and scales (outside the contract).
+ * nothing is launched and the outputs are untouched.  Inputs with NaN or Inf,
+ * and SwiGLU inputs whose product silu(gate) * up overflows fp32, give
+ * unspecified codes and scales (outside the contract; no fault).
  */
 #ifndef TK_QUANT_H
 #define TK_QUANT_H
@@ -106,7 +108,9 @@ tk_status tk_per_token_cast(const void *x, int64_t rows, int64_t cols, int64_t x
  * The first call on a device builds the library's correctly rounded silu32
  * table on that device (a one-time kernel followed by a wait on `stream`);
  * call tk_prepare_device() beforehand to keep that wait out of a region that
- * must not synchronise (e.g. graph capture).
+ * must not synchronise.  While `stream` is being captured into a graph and
+ * the table is not yet built, the call returns TK_ERROR_UNSUPPORTED without
+ * enqueueing anything.  A failed build is retried by the next call.
  */
 tk_status tk_swiglu_per_token_cast(const void *gate_up, int64_t rows, int64_t cols, int64_t x_ld,
                                    void *q, int64_t q_ld, void *scales, int64_t s_ld,
@@ -115,8 +119,8 @@ tk_status tk_swiglu_per_token_cast(const void *gate_up, int64_t rows, int64_t co
 
 /*
  * tk_per_token_cast_f32 -- the per-token cast of fp32 activations ("TileKernels"
- * (aiwiki.ai), Quantization: casts between BF16 or FP32 activations and
- * low-precision formats).  Identical to tk_per_token_cast except that x is
+ * (aiwiki.ai), Quantization: the casts accept FP32 activations as well as
+ * BF16).  Identical to tk_per_token_cast except that x is
  * fp32 [rows, cols] with row stride x_ld elements (x and 4*x_ld multiples of
  * 16 bytes) and is used as it is (no widening).  Rows whose scale row exceeds
  * 32 KiB (more than 8192 scale words) return TK_ERROR_UNSUPPORTED.
@@ -150,7 +154,7 @@ tk_status tk_per_token_dequant(const void *q, int64_t rows, int64_t cols, int64_
                                void *stream);
 
 /*
- * tk_per_token_cast_back -- per-token cast-and-cast-back ("TileKernels"
+ * tk_per_token_cast_back -- the cast-and-cast-back ("TileKernels"
  * (aiwiki.ai), Version 2.0.0): y = bf16 of the dequantized per-token cast of
  * x, bit-identical to tk_per_token_cast followed by tk_per_token_dequant with
  * TK_OUT_BF16, in one pass with no codes or scales written to memory.
@@ -216,7 +220,7 @@ tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t
 
 /*
  * tk_rmsnorm -- RMSNorm forward ("TileKernels" (aiwiki.ai), Version 2.0.0:
- * RMSNorm forward, with an optional fused FP8 cast).  For each row of C
+ * RMSNorm forward, which can be followed by an FP8 cast in the same kernel).  For each row of C
  * values, with a per-channel weight w (or none, i.e. all ones) and eps > 0:
  *     ss  = sum_j x_j^2, the exact sum rounded once to fp32 (nearest-even)
  *     t   = fl32(fl32(ss / C) + eps)
@@ -284,8 +288,9 @@ tk_status tk_stream_rw(const void *src, int64_t read_bytes, void *dst, int64_t w
 
 /*
  * tk_prepare_device -- build the per-device tables used by the SwiGLU form on
- * the current HIP device, and wait until they are ready.  Idempotent; safe to
- * call from several threads.
+ * the current HIP device (on the null stream), and wait until they are ready.
+ * Idempotent; safe to call from several threads; after a failure the next
+ * call tries again.
  */
 tk_status tk_prepare_device(void);
 

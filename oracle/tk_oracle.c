@@ -8,15 +8,14 @@
  * share no code, header, table or constant.
  *
  * What is computed, and where it comes from:
- *   - "Tile Kernels" (PyPI project page, v2.0.0), Features: per-token FP8/FP4
- *     casting of activations, with fused SwiGLU + quantization.
- *   - "TileKernels" (aiwiki.ai), section Quantization: scale-factor groups of
- *     16, 32, 64 or 128 channels, optional power-of-two rounding of the scale
- *     factors, optional packed UE8M0 scale factors; inputs are BF16
- *     activations.
+ *   - "Tile Kernels" (PyPI project page, v2.0.0), Features: activations are
+ *     cast per token to FP8 or FP4, and SwiGLU has a form fused with the cast.
+ *   - "TileKernels" (aiwiki.ai), section Quantization: each scale covers G
+ *     channels of a row, G one of 16, 32, 64, 128; scales may be rounded up
+ *     to powers of two and stored packed as UE8M0 bytes; the input is BF16.
  *   - "TileKernels, TileLang kernels for MoE routing and low-precision
  *     quantization" (hysenlabs.com), section "Seven kernel families": the
- *     activation function and the narrowing happen in one pass.
+ *     fused form computes SwiGLU and the cast in a single kernel.
  * The pages print no formula.  The one this oracle follows is the method's
  * fixed definition, step by step, for every row r and every group j of G
  * consecutive channels (columns jG .. jG+G-1):
@@ -32,11 +31,11 @@
  *      code, keeping the sign (also of zero);
  *   7. SwiGLU form: x_i is replaced by h_i = fl32(silu32(g_i) * u_i), where
  *      silu32(g) is the fp32 value nearest to g / (1 + e^-g).
- * Dequantization ("Tile Kernels" (PyPI, v2.0.0), Features: "casting and
- * dequantization") maps a code back to y = fl32(value(code) * s), returned as
- * fp32 or rounded to bf16 (nearest, ties to even); the per-token
- * cast-and-cast-back ("TileKernels" (aiwiki.ai), Version 2.0.0) is the cast
- * above followed by that dequantization, bf16 out.  The per-block and
+ * Dequantization ("Tile Kernels" (PyPI, v2.0.0), Features: the inverse of
+ * the cast) maps a code back to y = fl32(value(code) * s), returned as
+ * fp32 or rounded to bf16 (nearest, ties to even); the
+ * cast-and-cast-back ("TileKernels" (aiwiki.ai), Version 2.0.0) is the
+ * per-token cast above followed by that dequantization, bf16 out.  The per-block and
  * per-channel casts ("Tile Kernels" (PyPI, v2.0.0), Features) take step 1
  * over a block of rows x channels or over a whole column.  RMSNorm forward
  * with the optional fused cast ("TileKernels" (aiwiki.ai), Version 2.0.0) is
@@ -282,8 +281,8 @@ int oracle_swiglu_per_token_cast(const uint16_t *gate_up, int64_t rows, int64_t 
 
 /* ---- per-block and per-channel casts ---------------------------------- */
 
-/* "Tile Kernels" (PyPI, v2.0.0), Features: per-block and per-channel FP8/FP4
- * casting.  The same steps 1-6 with the amax taken over a block of
+/* "Tile Kernels" (PyPI, v2.0.0), Features: the cast also comes with one
+ * scale per block of rows x channels, or one per column.  The same steps 1-6 with the amax taken over a block of
  * block_rows x block_cols elements: rows [bi*Br, min(rows, (bi+1)*Br)) and
  * columns [bj*Bc, (bj+1)*Bc).  The last block row may be partial; cols must be
  * a multiple of Bc.  scales: fp32 [ceil(rows/Br), cols/Bc], or UE8M0 bytes of
@@ -414,8 +413,8 @@ int oracle_per_token_cast_back(const uint16_t *x, int64_t rows, int64_t cols, in
 
 /* ---- RMSNorm forward, alone and followed by the per-token cast -------- */
 
-/* "TileKernels" (aiwiki.ai), Version 2.0.0: RMSNorm forward, with an
- * optional fused FP8 cast.  The pages name the operation only; this is the
+/* "TileKernels" (aiwiki.ai), Version 2.0.0: RMSNorm forward, which can be
+ * followed by an FP8 cast in the same kernel.  The pages name the operation only; this is the
  * textbook root-mean-square normalisation of a row of C values with a
  * per-channel weight w (bf16, or none = all ones) and eps > 0:
  *   ss  = sum_j x_j^2, the exact sum rounded once to fp32 (nearest-even);

@@ -79,3 +79,51 @@ def test_graph_replays_match_eager():
         got = flat(graphed)
         for i, (a, b) in enumerate(zip(got, want)):
             assert np.array_equal(a, b), f"replay {rep}: output {i} differs from the eager run"
+
+
+_CAPTURE_CHILD = r'''
+import sys
+import torch
+sys.path.insert(0, sys.argv[1])
+import activation_quantization_token_amd as tk
+from activation_quantization_token_amd import rawcall
+lib = tk.load_library()
+rows, cols = 4, 128
+gu = torch.ones((rows, 2 * cols), dtype=torch.bfloat16, device="cuda")
+q, s = tk.empty_outputs(rows, cols, 128, "e4m3", "f32", gu.device)
+side = torch.cuda.Stream()
+torch.cuda.synchronize()
+fn, args = rawcall.prepare(lib, "tk_swiglu_per_token_cast",
+                           (gu.data_ptr(), rows, cols, 2 * cols, q.data_ptr(), cols, s.data_ptr(), 1, 128, 0, 1, 0,
+                            side.cuda_stream), {"gate_up": gu, "q": q, "scales": s})
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.stream(side):
+    graph.capture_begin()
+    during = fn(*args)                      # the table is not built yet: refused, nothing enqueued
+    graph.capture_end()
+print("during capture:", during, flush=True)
+print("prepare:", lib.tk_prepare_device(), flush=True)
+after = fn(*args)
+torch.cuda.synchronize()
+print("after:", after, flush=True)
+'''
+
+
+def test_table_build_refused_inside_a_capture(tmp_path):
+    """A fresh process whose silu32 table is not built yet: a SwiGLU call on a
+    stream being captured returns TK_ERROR_UNSUPPORTED and records nothing;
+    after the capture, tk_prepare_device builds the table and the same call
+    runs."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    log("[gpu] SwiGLU first call inside a graph capture (child process)")
+    script = tmp_path / "capture_child.py"
+    script.write_text(_CAPTURE_CHILD)
+    r = subprocess.run([sys.executable, str(script), root], capture_output=True, text=True, timeout=100)
+    assert r.returncode == 0, r.stdout + r.stderr[-3000:]
+    lines = dict(l.split(":", 1) for l in r.stdout.splitlines() if ":" in l)
+    assert lines["during capture"].strip() == "2", r.stdout           # TK_ERROR_UNSUPPORTED
+    assert lines["prepare"].strip() == "0", r.stdout
+    assert lines["after"].split()[0] == "0", r.stdout

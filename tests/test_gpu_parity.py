@@ -199,6 +199,37 @@ def test_cast_run_lengths(rows, cols, group, dt, p2, sf):
     check(x, group, dt, p2, sf, label="run-lengths")
 
 
+@pytest.mark.parametrize("rows,cols,group,dt,p2,sf,fp32", [
+    (255, 7168, 128, "e4m3", True, "f32", False),     # under one group of 8 runs of 32 rows: own order
+    (256, 7168, 128, "e4m3", True, "f32", False),     # exactly one group
+    (2049, 7168, 32, "e2m1", True, "ue8m0", False),   # 8 groups and one row
+    (4607, 7168, 32, "e4m3", True, "ue8m0", False),   # above 56 MiB: runs of 64 rows, a 511-row tail
+    (4609, 3584, 64, "e2m1", False, "f32", False),    # 7 KiB rows: runs of 64 rows, one row over
+    (1031, 7168, 16, "e4m3", True, "f32", True),      # fp32 rows: runs of 16, a 7-row tail
+    (4100, 7168, 32, "e2m1", True, "ue8m0", True),    # fp32 above 56 MiB: runs of 32, a 4-row tail
+])
+def test_row_order_across_xcds(rows, cols, group, dt, p2, sf, fp32):
+    """The row casts renumber their workgroups so that each XCD takes runs of
+    consecutive rows; row counts on and around the edges of those groups,
+    with guarded outputs: every row written once, and right."""
+    if not fp32:
+        x = inputs.generate_small(rows + cols, rows, cols, "student_t3" if rows % 2 else "normal")
+        check(x, group, dt, p2, sf, label="xcd-order")
+        return
+    x = inputs.generate_small_f32(rows + group, rows, cols)
+    log(f"[gpu] xcd-order fp32 rows={rows} cols={cols} G={group} {dt} pow2={p2} {sf}")
+    q = Guarded(rows, cols if dt == "e4m3" else cols // 2, torch.uint8, 24)
+    s = Guarded(rows, cols // group if sf == "f32" else cols // group // 4,
+                torch.float32 if sf == "f32" else torch.int32, 3)
+    tk.per_token_cast(torch.from_numpy(x).cuda(), group, dt, p2, sf, out=(q.view, s.view))
+    torch.cuda.synchronize()
+    wq, ws = oracle.per_token_cast_f32(x, group, dt, p2, sf)
+    assert q.canaries_intact() and s.canaries_intact()
+    got_q, got_s = q.view.cpu().numpy(), s.view.cpu().numpy()
+    assert np.array_equal(got_q, wq), first_mismatch(got_q, wq)
+    assert np.array_equal(got_s.view(np.uint32), ws.view(np.uint32))
+
+
 def test_swiglu_every_gate_pattern():
     """Every finite bf16 gate appears once; the up value is 0.5 next to gates
     beyond 2^100 so that h stays finite."""
