@@ -178,11 +178,6 @@ def cpu_baseline(w, x_bits, threads: int, op: str = "cast", block=(128, 128), we
     d1 = time.perf_counter() - t1
     one_bytes = bytes_per_row * (one.shape[0] if op != "per_channel" else sample) * \
         (1 if op != "per_channel" else one.shape[1] / w.cols)
-    model = ""
-    try:
-        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
-    except (OSError, StopIteration):
-        pass
     return {
         "value": round(passes * nbytes / dt / 1e9, 3),
         "unit": "GB/s",
@@ -193,16 +188,61 @@ def cpu_baseline(w, x_bits, threads: int, op: str = "cast", block=(128, 128), we
         "tokens_per_s": round(passes * sample / dt, 1),
         "single_core": {"value": round(p1 * one_bytes / d1 / 1e9, 4), "unit": "GB/s",
                         "sample": f"{p1} passes over one thread's share, {d1:.2f} s"},
-        "cpu_model": model,
+        **cpu_host(),
     }
+
+
+def settle_clocks(step, stream, target_ms: float) -> dict:
+    """Run `step` back to back for at least `target_ms` of GPU time (estimated
+    from 3 timed launches, then measured): the MI355X memory clocks reach
+    their steady state only after ~10-15 ms of sustained load, so a short
+    warm-up alone leaves the first timed launches slower."""
+    import math
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(3):
+        step()
+    b.record(stream)
+    b.synchronize()
+    per_ms = max(a.elapsed_time(b) / 3, 1e-3)
+    n = max(1, math.ceil(target_ms / per_ms))
+    a.record(stream)
+    for _ in range(n):
+        step()
+    b.record(stream)
+    b.synchronize()
+    return {"launches": n + 3, "ms": round(a.elapsed_time(b) + 3 * per_ms, 2), "target_ms": target_ms}
+
+
+def cpu_host() -> dict:
+    """What the host's /proc/cpuinfo says of its processor, and its core counts."""
+    fields = {}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if ":" not in line:
+                if fields:
+                    break                       # the first processor's block is enough
+                continue
+            k, v = (t.strip() for t in line.split(":", 1))
+            if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                fields[k] = v
+    except OSError:
+        pass
+    name = fields.get("model name", "")
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    return {"cpu_model": f"{name} ({ids})" if ids else name,
+            "host_cores_affinity": len(os.sched_getaffinity(0)), "host_cpu_count": os.cpu_count()}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps; HBM and fabric clocks need ~15 ms of sustained load to settle")
+    ap.add_argument("--warmup", type=int, default=300, help="untimed steps before the timed ones")
+    ap.add_argument("--settle-ms", type=float, default=30.0,
+                    help="back-to-back launches of the same call, at least this long in GPU time, before "
+                         "the warm-up: the memory clocks need ~10-15 ms of sustained load to settle")
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--op", choices=["cast", "cast_f32", "dequant", "cast_back", "per_block", "per_channel", "rmsnorm",
                                      "rmsnorm_cast"], default="cast",
@@ -234,7 +274,7 @@ def main():
     import numpy as np
     import torch
     import activation_quantization_token_amd as tk
-    from activation_quantization_token_amd import inputs
+    from activation_quantization_token_amd import inputs, rawcall
 
     w = inputs.WORKLOADS[args.workload]
     log(f"[bench] workload {w.index}: {w.name}; generating inputs")
@@ -329,29 +369,35 @@ def main():
     qd, sf, p2 = {"e4m3": 0, "e2m1": 1}[w.out_dtype], {"f32": 0, "ue8m0": 1}[w.scale_fmt], int(w.round_pow2)
 
     def raw_call(xi, qi, si, yi):
+        """(entry point, arguments, {pointer parameter: owning tensor}) of the step's call."""
         r, c = w.rows, w.cols
         if args.op in ("cast", "cast_f32"):
-            fn = (lib.tk_swiglu_per_token_cast if w.swiglu else
-                  lib.tk_per_token_cast_f32 if args.op == "cast_f32" else lib.tk_per_token_cast)
-            return fn, (xi.data_ptr(), r, c, xi.stride(0), qi.data_ptr(), qi.stride(0), si.data_ptr(), si.stride(0),
-                        w.group, qd, p2, sf, sh)
+            name = ("tk_swiglu_per_token_cast" if w.swiglu else
+                    "tk_per_token_cast_f32" if args.op == "cast_f32" else "tk_per_token_cast")
+            return name, (xi.data_ptr(), r, c, xi.stride(0), qi.data_ptr(), qi.stride(0), si.data_ptr(),
+                          si.stride(0), w.group, qd, p2, sf, sh), {"gate_up" if w.swiglu else "x": xi, "q": qi,
+                                                                   "scales": si}
         if args.op == "dequant":
-            return lib.tk_per_token_dequant, (qi.data_ptr(), r, c, qi.stride(0), si.data_ptr(), si.stride(0), w.group,
-                                              qd, sf, yi.data_ptr(), yi.stride(0), 0, sh)
+            return "tk_per_token_dequant", (qi.data_ptr(), r, c, qi.stride(0), si.data_ptr(), si.stride(0), w.group,
+                                            qd, sf, yi.data_ptr(), yi.stride(0), 0, sh), {"q": qi, "scales": si,
+                                                                                           "y": yi}
         if args.op == "cast_back":
-            return lib.tk_per_token_cast_back, (xi.data_ptr(), r, c, xi.stride(0), yi.data_ptr(), yi.stride(0),
-                                                w.group, qd, p2, sh)
+            return "tk_per_token_cast_back", (xi.data_ptr(), r, c, xi.stride(0), yi.data_ptr(), yi.stride(0),
+                                              w.group, qd, p2, sh), {"x": xi, "y": yi}
         if args.op == "per_block":
-            return lib.tk_per_block_cast, (xi.data_ptr(), r, c, xi.stride(0), qi.data_ptr(), qi.stride(0),
-                                           si.data_ptr(), si.stride(0), br, bc, qd, p2, sf, sh)
+            return "tk_per_block_cast", (xi.data_ptr(), r, c, xi.stride(0), qi.data_ptr(), qi.stride(0),
+                                         si.data_ptr(), si.stride(0), br, bc, qd, p2, sf, sh), {"x": xi, "q": qi,
+                                                                                                "scales": si}
         if args.op == "rmsnorm":
-            return lib.tk_rmsnorm, (xi.data_ptr(), r, c, xi.stride(0), wt.data_ptr(), 1e-6, yi.data_ptr(),
-                                    yi.stride(0), 0, sh)
+            return "tk_rmsnorm", (xi.data_ptr(), r, c, xi.stride(0), wt.data_ptr(), 1e-6, yi.data_ptr(),
+                                  yi.stride(0), 0, sh), {"x": xi, "weight": wt, "y": yi}
         if args.op == "rmsnorm_cast":
-            return lib.tk_rmsnorm_cast, (xi.data_ptr(), r, c, xi.stride(0), wt.data_ptr(), 1e-6, qi.data_ptr(),
-                                         qi.stride(0), si.data_ptr(), si.stride(0), w.group, qd, p2, sf, sh)
-        return lib.tk_per_channel_cast, (xi.data_ptr(), r, c, xi.stride(0), qi.data_ptr(), qi.stride(0), si.data_ptr(),
-                                         ws.data_ptr(), ws.numel(), qd, p2, sf, sh)
+            return "tk_rmsnorm_cast", (xi.data_ptr(), r, c, xi.stride(0), wt.data_ptr(), 1e-6, qi.data_ptr(),
+                                       qi.stride(0), si.data_ptr(), si.stride(0), w.group, qd, p2, sf, sh), \
+                {"x": xi, "weight": wt, "q": qi, "scales": si}
+        return "tk_per_channel_cast", (xi.data_ptr(), r, c, xi.stride(0), qi.data_ptr(), qi.stride(0), si.data_ptr(),
+                                       ws.data_ptr(), ws.numel(), qd, p2, sf, sh), {"x": xi, "q": qi, "scales": si,
+                                                                                    "workspace": ws}
 
     out_idx = (3,) if args.op in ("dequant", "cast_back", "rmsnorm") else (1, 2)
     calls = []
@@ -361,7 +407,8 @@ def main():
         want = [st[i].clone() for i in out_idx]
         for i in out_idx:
             st[i].view(torch.uint8).fill_(0xA5)
-        cfn, a = raw_call(*st)
+        # every pointer's extent, from the call's own arguments, inside its tensor
+        cfn, a = rawcall.prepare(lib, *raw_call(*st))
         if cfn(*a) != 0:
             raise SystemExit(f"raw {args.op} call failed")
         torch.cuda.synchronize()
@@ -376,6 +423,9 @@ def main():
             raise SystemExit(f"{args.op} launch failed")
         counter[0] += 1
 
+    stream = torch.cuda.current_stream(dev)
+    settle = settle_clocks(step, stream, args.settle_ms)
+    log(f"[bench] clock settle: {settle['launches']} launches, {settle['ms']} ms")
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
@@ -383,7 +433,6 @@ def main():
 
     # Timed region: K back-to-back launches on the current stream between two
     # events; the per-launch kernel time is the span over K.
-    stream = torch.cuda.current_stream(dev)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} steps over {len(sets)} buffer sets")
     torch.cuda.synchronize()
@@ -433,9 +482,16 @@ def main():
     csrc = [torch.empty(rd, dtype=torch.uint8, device=dev) for _ in range(len(sets))]
     cdst = [torch.empty(wr, dtype=torch.uint8, device=dev) for _ in range(len(sets))]
     tk.stream_rw(csrc[0], rd, cdst[0], wr)          # argument checks, once
-    rw_args = [(csrc[i].data_ptr(), rd, cdst[i].data_ptr(), wr, sh) for i in range(len(sets))]
+    rw_args = [rawcall.prepare(lib, "tk_stream_rw", (csrc[i].data_ptr(), rd, cdst[i].data_ptr(), wr, sh),
+                               {"src": csrc[i], "dst": cdst[i]})[1] for i in range(len(sets))]
+    rw_count = [0]
+
+    def rw_step():
+        lib.tk_stream_rw(*rw_args[rw_count[0] % len(sets)])
+        rw_count[0] += 1
+    settle_clocks(rw_step, stream, args.settle_ms)
     for i in range(args.warmup):
-        lib.tk_stream_rw(*rw_args[i % len(sets)])
+        rw_step()
     torch.cuda.synchronize()
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0.record(stream)
@@ -466,12 +522,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32",                 # the arithmetic: amax, scale and x / s in fp32
+        "settle": settle,
         "data": "synthetic",
         "config": {
             "workload": w.name, "rows": w.rows, "cols": w.cols, "group": w.group,
             "out_dtype": w.out_dtype, "round_pow2": w.round_pow2, "scale_fmt": w.scale_fmt,
             "swiglu": w.swiglu, "seed": w.seed, "bytes_per_step": nbytes, "op": args.op,
+            "input_dtype": "f32" if args.op == "cast_f32" else "bf16",
+            "code_format": "bf16" if args.op in ("cast_back", "rmsnorm") else w.out_dtype,
             **({"block": args.block} if args.op == "per_block" else {}),
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -503,6 +562,8 @@ def main():
             tk.copy_stream(src, dst)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
+        # at most 16 threads: a one-GPU machine's share of the host, whatever the
+        # affinity mask shows (both counts are reported)
         threads = min(16, len(os.sched_getaffinity(0)))
         log(f"[bench] CPU baseline: oracle on {threads} threads")
         weight_bits = None
