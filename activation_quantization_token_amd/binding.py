@@ -11,6 +11,7 @@ raises.
 from __future__ import annotations
 
 import ctypes
+import os
 import pathlib
 import threading
 
@@ -38,12 +39,17 @@ class TkError(RuntimeError):
 
 
 def load_library(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
-    """Load (once) and return the HIP library; raises if it is not built."""
+    """Load (once) and return the HIP library; raises if it is not built.
+    Without `path`, TK_QUANT_LIBRARY names another build of the same sources
+    (e.g. one with sanitized host code), else libtk_quant.so next to this file."""
     global _lib_handle
     with _lock:
         if _lib_handle is not None and path is None:
             return _lib_handle
-        p = pathlib.Path(path) if path is not None else LIB_PATH
+        if path is not None:
+            p = pathlib.Path(path)
+        else:
+            p = pathlib.Path(os.environ.get("TK_QUANT_LIBRARY") or LIB_PATH)
         if not p.exists():
             raise RuntimeError(
                 f"{p} is not built; run `python -m activation_quantization_token_amd.build`")

@@ -90,9 +90,16 @@ def _open(path) -> ctypes.CDLL:
 
 
 def _lib():
+    """The oracle library: TK_ORACLE_LIBRARY names another build of tk_oracle.c
+    (the sanitizer test's), else libtk_oracle.so, rebuilt when older than the
+    source."""
     global _handle
     with _lock:
         if _handle is None:
+            other = os.environ.get("TK_ORACLE_LIBRARY")
+            if other:
+                _handle = _open(other)
+                return _handle
             if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
                 build()
             _handle = _open(_LIB)
