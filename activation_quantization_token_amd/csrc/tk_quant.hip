@@ -469,15 +469,13 @@ struct DequantParams {
     int64_t s_ld;
     void *y;
     int64_t y_ld;        // elements of y's type
-    int32_t xcd_log2;    // xcd_order run length over the workgroups (-1: none)
 };
 
 template <int G, int QD, int SF, bool OUT_F32, int U, int WPB>
 __global__ __launch_bounds__(kWave * WPB) void dequant_kernel(DequantParams p)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = xcd_order(blockIdx.x, gridDim.x, p.xcd_log2) * WPB +
-                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wave = int64_t(blockIdx.x) * WPB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = int64_t(gridDim.x) * WPB;
     const int64_t nseg = (p.cols + kSegCols - 1) / kSegCols;
     const int64_t runs = (nseg + U - 1) / U;
@@ -908,17 +906,18 @@ DequantTable make_dequant_table()
 
 bool valid_group(int32_t g) { return g == 16 || g == 32 || g == 64 || g == 128; }
 
-// params points to the kernel's parameter struct, xcd_log2 to its run-length
-// field; wg_bytes: the bytes one workgroup's units read or write, whichever
-// is more.
-tk_status launch_unit_grid(const void *fn, int64_t rows, int64_t cols, void *params, int32_t &xcd_log2,
+// params points to the kernel's parameter struct; xcd_log2, if given, to its
+// run-length field, set for workgroups that read wg_bytes of input each.
+// Measured on MI355X at 32768 x 7168: the cast-and-cast-back 1.2 % faster in
+// XCD order, dequantization 0.8 % slower (it keeps its order).
+tk_status launch_unit_grid(const void *fn, int64_t rows, int64_t cols, void *params, int32_t *xcd_log2,
                            int64_t wg_bytes, hipStream_t s)
 {
     const int64_t nseg = (cols + kSegCols - 1) / kSegCols;
     const int64_t units = rows * ((nseg + kCastU - 1) / kCastU);
     const int64_t need = (units + kCastWPB - 1) / kCastWPB;
     const int64_t blocks = need > int64_t(0x7FFFFFFF) ? int64_t(0x7FFFFFFF) : need;   // the kernels loop
-    xcd_log2 = xcd_run_log2(need, blocks, wg_bytes);
+    if (xcd_log2) *xcd_log2 = xcd_run_log2(need, blocks, wg_bytes);
     void *args[] = {params};
     if (hipLaunchKernel(fn, dim3(uint32_t(blocks)), dim3(kWave * kCastWPB), args, 0, s) != hipSuccess)
         return TK_ERROR_LAUNCH;
@@ -1004,7 +1003,7 @@ tk_status tk_per_token_cast_back(const void *x, int64_t rows, int64_t cols, int6
     static const BackTable table = make_back_table();
     BackParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint16_t *>(y), y_ld, -1};
     return launch_unit_grid(reinterpret_cast<const void *>(table.fn[group_index(group)][out_dtype][round_pow2 ? 1 : 0]),
-                            rows, cols, &p, p.xcd_log2, int64_t(kCastWPB) * kCastU * kSegCols * 2,
+                            rows, cols, &p, &p.xcd_log2, int64_t(kCastWPB) * kCastU * kSegCols * 2,
                             static_cast<hipStream_t>(stream));
 }
 
@@ -1034,10 +1033,10 @@ tk_status tk_per_token_dequant(const void *q, int64_t rows, int64_t cols, int64_
     tk_status st = device_info(&dev, &info);
     if (st != TK_SUCCESS) return st;
     static const DequantTable table = make_dequant_table();
-    DequantParams p{static_cast<const uint8_t *>(q), rows, cols, q_ld, scales, s_ld, y, y_ld, -1};
+    DequantParams p{static_cast<const uint8_t *>(q), rows, cols, q_ld, scales, s_ld, y, y_ld};
     const DequantFn fn = table.fn[group_index(group)][in_dtype][scale_fmt][y_dtype == TK_OUT_F32 ? 1 : 0];
-    return launch_unit_grid(reinterpret_cast<const void *>(fn), rows, cols, &p, p.xcd_log2,
-                            int64_t(kCastWPB) * kCastU * kSegCols * ysize, static_cast<hipStream_t>(stream));
+    return launch_unit_grid(reinterpret_cast<const void *>(fn), rows, cols, &p, nullptr, 0,
+                            static_cast<hipStream_t>(stream));
 }
 
 tk_status tk_silu32_bf16(const void *g, void *out, int64_t n, void *stream)

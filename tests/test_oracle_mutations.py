@@ -123,3 +123,17 @@ def test_planted_mistake_is_caught(tmp_path, name, old, new, occ):
                 caught = e
                 break
     assert caught is not None, f"no pin caught the planted mistake: {name}"
+
+
+@pytest.mark.parametrize("name", ["scale by reciprocal multiply", "no amax floor", "floor 1e-3"])
+def test_workload_division_pin_alone_catches(tmp_path, name):
+    """The division pin on the five workloads' amax values fails, by itself,
+    for an inexact scale division or a wrong or missing floor.  (x * (1/s) in
+    the cast's own loop changes a code only at rounding edges, which the
+    division-hard groups of test_whole_tensor_division_hard_cases construct.)"""
+    _, old, new, occ = next(m for m in MUTATIONS if m[0] == name)
+    src = tmp_path / "mutant.c"
+    src.write_text(SRC.read_text().replace(old, new))
+    lib = oracle.compile_source(src, tmp_path / "libmutant.so")
+    with oracle.using(lib), pytest.raises(AssertionError):
+        pins.test_division_on_workload_amax_values()

@@ -206,6 +206,64 @@ def test_division_vs_exact_and_numpy():
         assert f32_bits(got) == f32_bits(want), (xi, si)
 
 
+def _workload_groups(rows=192, per_workload=4096, seed=17):
+    """Groups sampled from each of the five workloads' inputs (their own group
+    size, `rows` rows of each recipe; for the SwiGLU workload the groups of
+    h = fl32(silu32(g) * u), silu32 pinned against 60-digit decimals below):
+    a list of (workload index, fp32 group elements [n, G])."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for w in inputs.WORKLOADS:
+        bits = inputs.generate(w, rows=rows)
+        if w.swiglu:
+            vals = (oracle.silu32(widen(bits[:, :w.cols])) * widen(bits[:, w.cols:])).astype(np.float32)
+        else:
+            vals = widen(bits)
+        groups = vals.reshape(-1, w.group)
+        pick = rng.choice(groups.shape[0], min(per_workload, groups.shape[0]), replace=False)
+        out.append((w.index, groups[pick]))
+    return out
+
+
+def test_division_on_workload_amax_values():
+    """Both divisions of the cast on the amax values the five workloads produce
+    (19,456 groups, over 10^4): s = fl32(max(a, 1e-4) / D) for D = 448 and 6,
+    and v = fl32(x / s) for every element x of each group, against numpy's
+    float32 division everywhere and exact rationals on every scale and on a
+    random sample of 20,000 elements; and the whole cast of those groups
+    against the library composition."""
+    rng = random.Random(23)
+    groups = _workload_groups()
+    assert sum(g.shape[0] for _, g in groups) >= 10_000
+    floor = np.float32(1e-4)
+    for dt, D in (("e4m3", 448), ("e2m1", 6)):
+        pairs = []
+        for _, g in groups:
+            amax = np.max(np.abs(g), axis=1)
+            s, _ = oracle.group_scale(amax, dt, False)
+            want = (np.maximum(amax, floor) / np.float32(D)).astype(np.float32)
+            assert np.array_equal(s.view(np.uint32), want.view(np.uint32)), dt
+            for a, si in zip(amax.tolist(), s.tolist()):
+                exact = round_to_f32(Fraction(max(a, float(floor))) / D)
+                assert f32_bits(si) == f32_bits(exact), (dt, a)
+            flat = g.reshape(-1)
+            srep = np.repeat(s, g.shape[1])
+            got = oracle.divide(flat, srep)
+            want = (flat / srep).astype(np.float32)
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), dt
+            pairs.append((flat, srep, got))
+            # the whole cast on these groups against the library composition
+            q, sc = oracle.per_token_cast_f32(np.ascontiguousarray(g), g.shape[1], dt, False, "f32")
+            wq, ws = libref.cast_values(g, g.shape[1], dt, False, "f32")
+            assert np.array_equal(q, wq) and np.array_equal(sc.view(np.uint32), ws.view(np.uint32)), dt
+        for _ in range(10_000):
+            flat, srep, got = pairs[rng.randrange(len(pairs))]
+            i = rng.randrange(flat.size)
+            xi, si = float(flat[i]), float(srep[i])
+            want = round_to_f32(Fraction(xi) / Fraction(si), negative_zero=math.copysign(1, xi) < 0)
+            assert f32_bits(float(got[i])) == f32_bits(want), (dt, xi, si)
+
+
 # ---------------------------------------------------------------- silu32
 
 def test_silu32_every_bf16_gate_vs_60_digit_decimal():
