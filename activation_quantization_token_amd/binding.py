@@ -69,6 +69,10 @@ def load_library(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
         lib.tk_per_channel_workspace_bytes.restype = i64
         lib.tk_per_channel_cast.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, i64, i32, i32, i32, vp]
         lib.tk_per_channel_cast.restype = ctypes.c_int
+        lib.tk_per_channel_cast_noalloc.argtypes = [vp, i64, i64, i64, vp, i64, vp, i32, i32, i32, vp]
+        lib.tk_per_channel_cast_noalloc.restype = ctypes.c_int
+        lib.tk_per_channel_noalloc_max_workspace_bytes.argtypes = []
+        lib.tk_per_channel_noalloc_max_workspace_bytes.restype = i64
         f32 = ctypes.c_float
         lib.tk_rmsnorm.argtypes = [vp, i64, i64, i64, vp, f32, vp, i64, i32, vp]
         lib.tk_rmsnorm.restype = ctypes.c_int
@@ -340,6 +344,17 @@ def tk_per_channel_cast(x: int, rows: int, cols: int, x_ld: int, q: int, q_ld: i
     """Raw C call with integer pointers; returns the tk_status code."""
     return load_library().tk_per_channel_cast(x, rows, cols, x_ld, q, q_ld, scales, workspace, workspace_bytes,
                                               out_dtype, round_pow2, scale_fmt, stream)
+
+
+def tk_per_channel_cast_noalloc(x: int, rows: int, cols: int, x_ld: int, q: int, q_ld: int, scales: int,
+                                out_dtype: int, round_pow2: int, scale_fmt: int, stream: int) -> int:
+    """Raw C call with integer pointers (the library's static workspace); returns the tk_status code."""
+    return load_library().tk_per_channel_cast_noalloc(x, rows, cols, x_ld, q, q_ld, scales, out_dtype, round_pow2,
+                                                      scale_fmt, stream)
+
+
+def tk_per_channel_noalloc_max_workspace_bytes() -> int:
+    return int(load_library().tk_per_channel_noalloc_max_workspace_bytes())
 
 
 def _check_formats(out_dtype: str, scale_fmt: str):

@@ -441,6 +441,42 @@ tk_status validate_common(const void *x, int64_t rows, int64_t cols, int64_t x_l
     return TK_SUCCESS;
 }
 
+// The no-allocation variant's workspace: a file-scope array in device
+// memory, one copy per GPU, kept until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in);
+// it passes the device address that hipGetSymbolAddress gives, looked up once
+// per device with that device current.  Every no-allocation call on a GPU
+// shares that GPU's copy.
+constexpr int64_t kNoAllocScratchBytes = int64_t(1) << 20;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+struct ScratchSlot {
+    std::mutex mutex;
+    std::atomic<void *> ptr{nullptr};
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+tk_status scratch_address(int dev, void **out)
+{
+    ScratchSlot &slot = g_scratch[dev];
+    void *p = slot.ptr.load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(slot.mutex);
+        p = slot.ptr.load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TK_ERROR_DEVICE;
+            slot.ptr.store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return TK_SUCCESS;
+}
+
 int64_t channel_chunk_rows(int64_t rows)
 {
     const int64_t r = (rows + kChannelMaxChunks - 1) / kChannelMaxChunks;
@@ -451,6 +487,38 @@ int64_t channel_chunks(int64_t rows)
 {
     const int64_t cr = channel_chunk_rows(rows);
     return (rows + cr - 1) / cr;
+}
+
+// The two passes of the per-channel cast on an argument-checked call, with
+// `workspace` (device memory of at least tk_per_channel_workspace_bytes).
+tk_status launch_channel(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void *q, int64_t q_ld, void *scales,
+                         void *workspace, int32_t out_dtype, int32_t round_pow2, int32_t scale_fmt, hipStream_t s)
+{
+    static const ChannelTable table = make_channel_table();
+    const int variant = !round_pow2 ? 0 : (scale_fmt == kScaleF32 ? 1 : 2);
+    const int64_t chunk_rows = channel_chunk_rows(rows), chunks = channel_chunks(rows);
+    const int64_t stripes = (cols + kSegCols - 1) / kSegCols;
+    const int64_t tiles = chunks * stripes;
+    if (tiles > int64_t(0x7FFFFFFF)) return TK_ERROR_UNSUPPORTED;
+    ChannelParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld, scales,
+                    static_cast<uint16_t *>(workspace), chunk_rows, chunks};
+    void *args[] = {&p};
+    // Size classes of x.  Up to half the 256 MiB Infinity Cache the second
+    // pass uses ordinary loads (with inputs rotated over three buffer sets:
+    // -6 % at 4096 x 7168; at 16384 x 7168, 235 MB, ordinary loads were 4 %
+    // slower), non-temporal ones beyond; up to 64 MiB both passes keep 2 rows
+    // in flight per wave instead of 4 (-10 % at 4096 x 7168; 1 % slower at
+    // 8192 rows, 2-5 % at 16384 and 32768).
+    const int64_t x_bytes = rows * cols * 2;
+    const int pi = x_bytes <= kChannelSmallBytes ? 2 : x_bytes <= kChannelCachedBytes ? 1 : 0;
+    const void *amax_fn = pi == 2 ? reinterpret_cast<const void *>(channel_amax_kernel<kChannelSmallUnroll>)
+                                  : reinterpret_cast<const void *>(channel_amax_kernel<kChannelUnroll>);
+    if (hipLaunchKernel(amax_fn, dim3(uint32_t(tiles)), dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    if (hipLaunchKernel(reinterpret_cast<const void *>(table.cast[out_dtype][variant][pi]), dim3(uint32_t(tiles)),
+                        dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    return TK_SUCCESS;
 }
 
 }  // namespace
@@ -520,32 +588,30 @@ tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t
     DeviceInfo *info = nullptr;
     st = device_info(&dev, &info);
     if (st != TK_SUCCESS) return st;
-    static const ChannelTable table = make_channel_table();
-    const int variant = !round_pow2 ? 0 : (scale_fmt == kScaleF32 ? 1 : 2);
-    const int64_t chunk_rows = channel_chunk_rows(rows), chunks = channel_chunks(rows);
-    const int64_t stripes = (cols + kSegCols - 1) / kSegCols;
-    const int64_t tiles = chunks * stripes;
-    if (tiles > int64_t(0x7FFFFFFF)) return TK_ERROR_UNSUPPORTED;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    ChannelParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld, scales,
-                    static_cast<uint16_t *>(workspace), chunk_rows, chunks};
-    void *args[] = {&p};
-    // Size classes of x.  Up to half the 256 MiB Infinity Cache the second
-    // pass uses ordinary loads (with inputs rotated over three buffer sets:
-    // -6 % at 4096 x 7168; at 16384 x 7168, 235 MB, ordinary loads were 4 %
-    // slower), non-temporal ones beyond; up to 64 MiB both passes keep 2 rows
-    // in flight per wave instead of 4 (-10 % at 4096 x 7168; 1 % slower at
-    // 8192 rows, 2-5 % at 16384 and 32768).
-    const int64_t x_bytes = rows * cols * 2;
-    const int pi = x_bytes <= kChannelSmallBytes ? 2 : x_bytes <= kChannelCachedBytes ? 1 : 0;
-    const void *amax_fn = pi == 2 ? reinterpret_cast<const void *>(channel_amax_kernel<kChannelSmallUnroll>)
-                                  : reinterpret_cast<const void *>(channel_amax_kernel<kChannelUnroll>);
-    if (hipLaunchKernel(amax_fn, dim3(uint32_t(tiles)), dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
-        return TK_ERROR_LAUNCH;
-    if (hipLaunchKernel(reinterpret_cast<const void *>(table.cast[out_dtype][variant][pi]), dim3(uint32_t(tiles)),
-                        dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
-        return TK_ERROR_LAUNCH;
-    return TK_SUCCESS;
+    return launch_channel(x, rows, cols, x_ld, q, q_ld, scales, workspace, out_dtype, round_pow2, scale_fmt,
+                          static_cast<hipStream_t>(stream));
 }
+
+tk_status tk_per_channel_cast_noalloc(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void *q, int64_t q_ld,
+                                      void *scales, int32_t out_dtype, int32_t round_pow2, int32_t scale_fmt,
+                                      void *stream)
+{
+    if (cols <= 0 || cols % 8 != 0) return TK_ERROR_INVALID_VALUE;
+    tk_status st = validate_common(x, rows, cols, x_ld, q, q_ld, scales, out_dtype, round_pow2, scale_fmt);
+    if (st != TK_SUCCESS || rows == 0) return st;
+    if (tk_per_channel_workspace_bytes(rows, cols) > kNoAllocScratchBytes) return TK_ERROR_UNSUPPORTED;
+    if (!aligned(scales, scale_fmt == kScaleF32 ? 16 : 8)) return TK_ERROR_MISALIGNED;
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    st = device_info(&dev, &info);
+    if (st != TK_SUCCESS) return st;
+    void *ws = nullptr;
+    st = scratch_address(dev, &ws);
+    if (st != TK_SUCCESS) return st;
+    return launch_channel(x, rows, cols, x_ld, q, q_ld, scales, ws, out_dtype, round_pow2, scale_fmt,
+                          static_cast<hipStream_t>(stream));
+}
+
+int64_t tk_per_channel_noalloc_max_workspace_bytes(void) { return kNoAllocScratchBytes; }
 
 }  // extern "C"

@@ -34,6 +34,8 @@ SIGNATURES = {
                           "out_dtype", "round_pow2", "scale_fmt", "stream"),
     "tk_per_channel_cast": ("x", "rows", "cols", "x_ld", "q", "q_ld", "scales", "workspace", "workspace_bytes",
                             "out_dtype", "round_pow2", "scale_fmt", "stream"),
+    "tk_per_channel_cast_noalloc": ("x", "rows", "cols", "x_ld", "q", "q_ld", "scales", "out_dtype", "round_pow2",
+                                    "scale_fmt", "stream"),
     "tk_rmsnorm": ("x", "rows", "cols", "x_ld", "weight", "eps", "y", "y_ld", "y_dtype", "stream"),
     "tk_rmsnorm_cast": ("x", "rows", "cols", "x_ld", "weight", "eps", "q", "q_ld", "scales", "s_ld", "group",
                         "out_dtype", "round_pow2", "scale_fmt", "stream"),
@@ -92,11 +94,13 @@ def extents(name: str, args) -> dict:
         return {"x": _rows_span(rows, a["x_ld"], 2 * cols, 2),
                 "q": _rows_span(rows, a["q_ld"], _code_bytes(cols, a["out_dtype"]), 1),
                 "scales": _rows_span(nbr, a["s_ld"], 4 * _scale_words(cols // a["block_cols"], a["scale_fmt"]), 4)}
-    if name == "tk_per_channel_cast":
-        return {"x": _rows_span(rows, a["x_ld"], 2 * cols, 2),
-                "q": _rows_span(rows, a["q_ld"], _code_bytes(cols, a["out_dtype"]), 1),
-                "scales": 0 if rows <= 0 else 4 * _scale_words(cols, a["scale_fmt"]),
-                "workspace": a["workspace_bytes"]}
+    if name in ("tk_per_channel_cast", "tk_per_channel_cast_noalloc"):
+        out = {"x": _rows_span(rows, a["x_ld"], 2 * cols, 2),
+               "q": _rows_span(rows, a["q_ld"], _code_bytes(cols, a["out_dtype"]), 1),
+               "scales": 0 if rows <= 0 else 4 * _scale_words(cols, a["scale_fmt"])}
+        if name == "tk_per_channel_cast":
+            out["workspace"] = a["workspace_bytes"]
+        return out
     if name == "tk_rmsnorm":
         ysize = 4 if a["y_dtype"] == OUT_F32 else 2
         return {"x": _rows_span(rows, a["x_ld"], 2 * cols, 2), "weight": 2 * cols if a["weight"] else 0,

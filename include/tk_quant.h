@@ -219,6 +219,26 @@ tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t
                               int32_t round_pow2, int32_t scale_fmt, void *stream);
 
 /*
+ * tk_per_channel_cast_noalloc -- tk_per_channel_cast for callers that cannot
+ * allocate device memory or hand in a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, kernels and results as tk_per_channel_cast without the workspace
+ * pair: the column maxima go to the library's own static device array of
+ * tk_per_channel_noalloc_max_workspace_bytes() bytes (1 MiB: 32 chunks of
+ * cols <= 16384 columns), one per GPU, held until the process ends.  The call
+ * itself allocates nothing.  Inputs that need more than that
+ * (tk_per_channel_workspace_bytes(rows, cols) above the maximum) return
+ * TK_ERROR_UNSUPPORTED with nothing launched.  Every call on a GPU shares that
+ * GPU's array, so calls that may overlap on one GPU (different streams, or
+ * several host threads) race: order them on one stream.  Each call writes
+ * every workspace entry it reads, so nothing needs clearing between calls.
+ */
+tk_status tk_per_channel_cast_noalloc(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
+                                      void *q, int64_t q_ld, void *scales, int32_t out_dtype,
+                                      int32_t round_pow2, int32_t scale_fmt, void *stream);
+int64_t tk_per_channel_noalloc_max_workspace_bytes(void);
+
+/*
  * tk_rmsnorm -- RMSNorm forward ("TileKernels" (aiwiki.ai), Version 2.0.0:
  * RMSNorm forward, which can be followed by an FP8 cast in the same kernel).  For each row of C
  * values, with a per-channel weight w (or none, i.e. all ones) and eps > 0:

@@ -198,6 +198,23 @@ def test_per_channel_validation(kw, want):
                                   ws_bytes, a["out_dtype"], a["round_pow2"], a["scale_fmt"], 0) == want
 
 
+@pytest.mark.parametrize("kw,want", [
+    (dict(cols=12), INVALID), (dict(cols=0), INVALID), (dict(rows=-1), INVALID), (dict(out_dtype=2), INVALID),
+    (dict(scale_fmt=1, round_pow2=0), INVALID), (dict(x_ld=100), INVALID), (dict(x=0), INVALID), (dict(s=0), INVALID),
+    (dict(x=X + 8), MISALIGNED), (dict(s=S + 8), MISALIGNED),
+    (dict(rows=4096, cols=16392, x_ld=16392, q_ld=16392), UNSUPPORTED),    # column maxima above 1 MiB
+    (dict(rows=0, x=0, q=0, s=0), 0),
+])
+def test_per_channel_noalloc_validation(kw, want):
+    """Checks before anything is launched (the valid calls here stop at the
+    missing GPU, TK_ERROR_DEVICE, before the static workspace is looked up)."""
+    a = dict(x=X, rows=4, cols=256, x_ld=256, q=Q, q_ld=256, s=S, out_dtype=0, round_pow2=1, scale_fmt=0)
+    a.update(kw)
+    assert binding.tk_per_channel_cast_noalloc(a["x"], a["rows"], a["cols"], a["x_ld"], a["q"], a["q_ld"], a["s"],
+                                               a["out_dtype"], a["round_pow2"], a["scale_fmt"], 0) == want
+    assert binding.tk_per_channel_noalloc_max_workspace_bytes() == 1 << 20
+
+
 def test_per_channel_workspace_size():
     assert tk.tk_per_channel_workspace_bytes(0, 256) == 0
     assert tk.tk_per_channel_workspace_bytes(1, 256) == 256 * 2
