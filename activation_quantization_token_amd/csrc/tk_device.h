@@ -133,7 +133,10 @@ template <int QD, bool POW2>
 __device__ __forceinline__ Scale<QD, POW2> group_scale(uint32_t amax_bits)
 {
     constexpr float D = (QD == kE4M3) ? 448.0f : 6.0f;
-    const float a = fmaxf(__uint_as_float(amax_bits), 1e-4f);
+    // max(a, 1e-4f) on the bits: amax_bits is the pattern of a finite |x| >= 0,
+    // whose unsigned order is the numeric order (one integer max, where fmaxf
+    // would first canonicalise its operand)
+    const float a = __uint_as_float(max(amax_bits, 0x38D1B717u));   // 1e-4f
     Scale<QD, POW2> r;
     r.inv = 0.0f;
     r.e8 = 0;
