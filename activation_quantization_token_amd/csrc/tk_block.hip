@@ -1,6 +1,7 @@
 // tk_block.hip -- gfx950 kernels and C ABI for the per-block and per-channel
-// casts ("Tile Kernels" (PyPI, v2.0.0), Features: per-token, per-block and
-// per-channel FP8/FP4 casting).  The arithmetic is the per-token cast's
+// casts ("Tile Kernels" (PyPI, v2.0.0), Features: besides one scale per token
+// group, the casts come with one scale per block or per channel).  The
+// arithmetic is the per-token cast's
 // (include/tk_quant.h) with the |max| taken over a block of rows x channels,
 // or over a whole column.
 //

@@ -195,8 +195,8 @@ tk_status tk_per_block_cast(const void *x, int64_t rows, int64_t cols, int64_t x
 
 /*
  * tk_per_channel_cast -- the cast with one scale per column (channel), the
- * |max| taken over all rows ("Tile Kernels" (PyPI, v2.0.0), Features:
- * per-channel FP8/FP4 casting); otherwise exactly the arithmetic of
+ * |max| taken over all rows ("Tile Kernels" (PyPI, v2.0.0), Features: a scale
+ * per channel); otherwise exactly the arithmetic of
  * tk_per_token_cast.  Equal to tk_per_block_cast with block_rows = rows and
  * block_cols = 1.
  *
