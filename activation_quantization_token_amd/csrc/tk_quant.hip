@@ -352,6 +352,7 @@ __global__ __launch_bounds__(1024) void cast_rows_kernel(CastParams p)
 // 4096 rows, P = 2 3-5 % faster at 16384 and 32768).
 constexpr int kF32Cols = 256;              // columns per piece (one 1 KiB load per wave)
 constexpr int64_t kF32FewRows = 4096;
+constexpr int64_t kF32HalvesBytes = int64_t(512) << 20;
 
 // Max over the G/4 consecutive lanes that hold one group of a piece.
 template <int G>
@@ -378,25 +379,29 @@ __device__ __forceinline__ uint32_t encode4(const float (&v)[4])
     }
 }
 
-template <int G, int QD, bool POW2, int SF, int P>
+template <int G, int QD, bool POW2, int SF, int P, int PARTS = 1>
 __global__ __launch_bounds__(1024) void cast_rows_f32_kernel(CastParams p)
 {
-    extern __shared__ uint32_t row_scales[];     // the row's scale words
+    extern __shared__ uint32_t row_scales[];     // the part's scale words
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = int(blockDim.x) >> 6;
     const uint32_t cols = uint32_t(p.cols);
+    const uint32_t part_cols = cols / PARTS;     // whole runs and scale words (host-checked)
     constexpr uint32_t kRunCols = P * kF32Cols;
-    const int runs = int((cols + kRunCols - 1) / kRunCols);
-    const uint32_t s_words = SF == kScaleF32 ? cols / G : cols / G / 4;
+    const int runs = int((part_cols + kRunCols - 1) / kRunCols);
+    const uint32_t s_words = SF == kScaleF32 ? part_cols / G : part_cols / G / 4;
     constexpr int kLanesPerGroup = G / 4;
     const float *xf = reinterpret_cast<const float *>(p.x);
-    for (int64_t row = xcd_order(blockIdx.x, p.rows, p.xcd_log2); row < p.rows; row += gridDim.x) {
+    const int64_t items = p.rows * PARTS;
+    for (int64_t item = xcd_order(blockIdx.x, items, p.xcd_log2); item < items; item += gridDim.x) {
+        const int64_t row = item / PARTS;
+        const uint32_t c0 = uint32_t(item % PARTS) * part_cols;
         const __amdgpu_buffer_rsrc_t xrow = row_buffer(xf + row * p.x_ld, cols * 4u);
         __amdgpu_buffer_rsrc_t qrow, srow;
         output_rows<G, QD, SF>(p, row, qrow, srow);
         for (int run = wave; run < runs; run += nw) {
-            const uint32_t col0 = uint32_t(run) * kRunCols + uint32_t(lane) * 4u;
+            const uint32_t col0 = c0 + uint32_t(run) * kRunCols + uint32_t(lane) * 4u;
             u32x4 w[P];
 #pragma unroll
             for (int k = 0; k < P; ++k) w[k] = load16(xrow, (col0 + k * kF32Cols) * 4u);
@@ -414,13 +419,14 @@ __global__ __launch_bounds__(1024) void cast_rows_f32_kernel(CastParams p)
                 if constexpr (QD == kE4M3) store4(qrow, col, codes);
                 else __builtin_amdgcn_raw_buffer_store_b16(uint16_t(codes), qrow, int(col / 2), 0, kNonTemporal);
                 if ((lane % kLanesPerGroup) == 0 && col < cols) {
-                    if constexpr (SF == kScaleF32) row_scales[col / G] = __float_as_uint(sc.s);
-                    else reinterpret_cast<uint8_t *>(row_scales)[col / G] = uint8_t(sc.e8);
+                    if constexpr (SF == kScaleF32) row_scales[(col - c0) / G] = __float_as_uint(sc.s);
+                    else reinterpret_cast<uint8_t *>(row_scales)[(col - c0) / G] = uint8_t(sc.e8);
                 }
             }
         }
         __syncthreads();
-        for (uint32_t t = threadIdx.x; t < s_words; t += blockDim.x) store_scale(srow, t * 4u, row_scales[t]);
+        const uint32_t w0 = SF == kScaleF32 ? c0 / G : c0 / G / 4;   // the part's first scale word
+        for (uint32_t t = threadIdx.x; t < s_words; t += blockDim.x) store_scale(srow, (w0 + t) * 4u, row_scales[t]);
         __syncthreads();                         // the next row reuses row_scales
     }
 }
@@ -726,13 +732,13 @@ struct RowTable {
     CastFn fn[4][2][3];
 };
 
-template <int P, int G, int QD, int U>
+template <int P, int G, int QD, int U, int PARTS = 1>
 void fill_rows(CastFn (&t)[3])
 {
-    if constexpr (P > 0) {                       // fp32 input, P pieces per wave
-        t[0] = cast_rows_f32_kernel<G, QD, false, kScaleF32, P>;
-        t[1] = cast_rows_f32_kernel<G, QD, true, kScaleF32, P>;
-        t[2] = cast_rows_f32_kernel<G, QD, true, kScaleUE8M0, P>;
+    if constexpr (P > 0) {                       // fp32 input, P pieces per wave, PARTS workgroups per row
+        t[0] = cast_rows_f32_kernel<G, QD, false, kScaleF32, P, PARTS>;
+        t[1] = cast_rows_f32_kernel<G, QD, true, kScaleF32, P, PARTS>;
+        t[2] = cast_rows_f32_kernel<G, QD, true, kScaleUE8M0, P, PARTS>;
     } else {
         t[0] = cast_rows_kernel<G, QD, false, kScaleF32, U>;
         t[1] = cast_rows_kernel<G, QD, true, kScaleF32, U>;
@@ -742,14 +748,14 @@ void fill_rows(CastFn (&t)[3])
 
 // P = 0: the bf16 row kernel with runs of U segments; P > 0: the fp32 row
 // kernel with P pieces per wave.
-template <int P, int U = kCastU>
+template <int P, int U = kCastU, int PARTS = 1>
 RowTable make_row_table()
 {
     RowTable t;
-    fill_rows<P, 16, kE4M3, U>(t.fn[0][0]);  fill_rows<P, 16, kE2M1, U>(t.fn[0][1]);
-    fill_rows<P, 32, kE4M3, U>(t.fn[1][0]);  fill_rows<P, 32, kE2M1, U>(t.fn[1][1]);
-    fill_rows<P, 64, kE4M3, U>(t.fn[2][0]);  fill_rows<P, 64, kE2M1, U>(t.fn[2][1]);
-    fill_rows<P, 128, kE4M3, U>(t.fn[3][0]); fill_rows<P, 128, kE2M1, U>(t.fn[3][1]);
+    fill_rows<P, 16, kE4M3, U, PARTS>(t.fn[0][0]);  fill_rows<P, 16, kE2M1, U, PARTS>(t.fn[0][1]);
+    fill_rows<P, 32, kE4M3, U, PARTS>(t.fn[1][0]);  fill_rows<P, 32, kE2M1, U, PARTS>(t.fn[1][1]);
+    fill_rows<P, 64, kE4M3, U, PARTS>(t.fn[2][0]);  fill_rows<P, 64, kE2M1, U, PARTS>(t.fn[2][1]);
+    fill_rows<P, 128, kE4M3, U, PARTS>(t.fn[3][0]); fill_rows<P, 128, kE2M1, U, PARTS>(t.fn[3][1]);
     return t;
 }
 
@@ -977,15 +983,25 @@ tk_status tk_per_token_cast_f32(const void *x, int64_t rows, int64_t cols, int64
     if (st != TK_SUCCESS) return st;
     static const RowTable table4 = make_row_table<4>();
     static const RowTable table2 = make_row_table<2>();
+    static const RowTable table2h = make_row_table<2, kCastU, 2>();
     const bool few = rows <= kF32FewRows;
-    const RowTable &table = few ? table4 : table2;
     const int variant = !round_pow2 ? 0 : (scale_fmt == kScaleF32 ? 1 : 2);
     const int64_t run_cols = (few ? 4 : 2) * kF32Cols;
-    const int64_t runs = (cols + run_cols - 1) / run_cols;
+    // Two workgroups per row (7 waves each at 7168 columns, in XCD order over the
+    // halves) above kF32HalvesBytes of input, when each half is whole runs and
+    // whole scale words.  Measured on MI355X at 7168 columns against one
+    // 14-wave workgroup per row: -2.3 % at 32768 rows (940 MB), +0.7 % at
+    // 16384, -0.9 % at 8192, equal at 4097.
+    const int64_t word_cols = scale_fmt == kScaleF32 ? group : 4 * group;
+    const int parts = (rows * cols * 4 > kF32HalvesBytes && cols % (2 * run_cols) == 0 && (cols / 2) % word_cols == 0)
+                          ? 2 : 1;
+    const RowTable &table = few ? table4 : parts == 2 ? table2h : table2;
+    const int64_t runs = (cols / parts + run_cols - 1) / run_cols;
     const int waves = int(runs < kRowMaxWaves ? runs : kRowMaxWaves);
-    const int64_t blocks = rows < int64_t(0x7FFFFFFF) ? rows : int64_t(0x7FFFFFFF);
+    const int64_t items = rows * parts;
+    const int64_t blocks = items < int64_t(0x7FFFFFFF) ? items : int64_t(0x7FFFFFFF);
     CastParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld, scales,
-                 s_ld, xcd_run_log2(rows, blocks, cols * 4)};
+                 s_ld, xcd_run_log2(items, blocks, cols * 4 / parts)};
     void *args[] = {&p};
     const CastFn fn = table.fn[group_index(group)][out_dtype][variant];
     if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * waves), args,

@@ -398,6 +398,30 @@ def test_fp32_input_cast(group, dt, p2, sf, rows, extra):
     assert np.array_equal(got_s.view(np.uint32), ws.view(np.uint32))
 
 
+@pytest.mark.parametrize("rows,cols,group,dt,p2,sf", [(18725, 7168, 64, "e4m3", False, "f32"),
+                                                     (19001, 7168, 16, "e2m1", True, "ue8m0")])
+def test_fp32_input_cast_half_rows(rows, cols, group, dt, p2, sf):
+    """Above 512 MiB of fp32 input each row is cast by two workgroups, one per
+    half, in XCD order over the halves; odd row counts leave a ragged last
+    group.  The oracle checks the first and last 64 rows, every 37th row, and
+    the rows around every 32-row boundary of the XCD runs."""
+    x = inputs.generate_small_f32(rows + group, rows, cols)
+    log(f"[gpu] fp32-input cast, half rows: rows={rows} cols={cols} G={group} {dt} pow2={p2} {sf}")
+    q = Guarded(rows, cols if dt == "e4m3" else cols // 2, torch.uint8, 24)
+    s = Guarded(rows, cols // group if sf == "f32" else cols // group // 4,
+                torch.float32 if sf == "f32" else torch.int32, 3)
+    tk.per_token_cast(torch.from_numpy(x).cuda(), group, dt, p2, sf, out=(q.view, s.view))
+    torch.cuda.synchronize()
+    assert q.canaries_intact() and s.canaries_intact()
+    idx = set(range(64)) | set(range(rows - 64, rows)) | set(range(0, rows, 37))
+    idx |= {r for b in range(0, rows, 32) for r in (b - 1, b) if 0 <= r < rows}
+    idx = np.array(sorted(idx))
+    wq, ws = oracle.per_token_cast_f32(np.ascontiguousarray(x[idx]), group, dt, p2, sf)
+    got_q, got_s = q.view.cpu().numpy()[idx], s.view.cpu().numpy()[idx]
+    assert np.array_equal(got_q, wq), first_mismatch(got_q, wq)
+    assert np.array_equal(got_s.view(np.uint32), ws.view(np.uint32))
+
+
 @pytest.mark.parametrize("wi", [1, 4])
 def test_fp32_input_cast_full_size_sampled(wi):
     """The workload's input widened to fp32 (exact), cast at full size as the
