@@ -82,15 +82,15 @@ __device__ __forceinline__ bool certified(double d)
     return dist > 256u;
 }
 
-// Exact sum of squares of the row, rounded to fp32 by hand: integer digits
-// in LDS (64-bit atomic adds of 32-bit pieces, carries resolved at the end by
-// one thread).  Called by every thread of the workgroup.
-__device__ float exact_sum_squares(const u32x4 (&w)[kNormU], unsigned long long *acc, float *result)
+// Every square of the lane's N segments of 8 bf16 into the digit array:
+// |x| = M 2^k with an 8-bit integer M, so x^2 2^266 = M^2 2^(2k + 266) is an
+// integer of at most 16 bits at a non-negative bit position; its two 32-bit
+// pieces go to the digits they fall in with 64-bit LDS atomic adds.
+template <int N>
+__device__ __forceinline__ void add_squares_exact(const u32x4 (&w)[N], unsigned long long *acc)
 {
-    if (threadIdx.x < kExactDigits) acc[threadIdx.x] = 0ull;
-    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kNormU; ++k) {
+    for (int k = 0; k < N; ++k) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint32_t b = (w[k][i / 2] >> (16 * (i % 2))) & 0x7FFFu;
@@ -98,41 +98,58 @@ __device__ float exact_sum_squares(const u32x4 (&w)[kNormU], unsigned long long 
             if (b != 0u) {
                 const int kexp = e ? int(e) - 134 : -133;      // |x| = M * 2^kexp
                 const uint32_t M = e ? (m | 0x80u) : m;
-                const int p = 2 * kexp + kExactShift;           // >= 0
-                const uint64_t v = uint64_t(M * M) << (p & 31);
-                atomicAdd(&acc[p >> 5], (unsigned long long)(v & 0xFFFFFFFFull));
-                atomicAdd(&acc[(p >> 5) + 1], (unsigned long long)(v >> 32));
+                const int pos = 2 * kexp + kExactShift;         // >= 0
+                const uint64_t v = uint64_t(M * M) << (pos & 31);
+                atomicAdd(&acc[pos >> 5], (unsigned long long)(v & 0xFFFFFFFFull));
+                atomicAdd(&acc[(pos >> 5) + 1], (unsigned long long)(v >> 32));
             }
         }
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t dig[kExactDigits];
-        uint64_t carry = 0;
-        for (int i = 0; i < kExactDigits; ++i) {
-            const uint64_t t = acc[i] + carry;
-            dig[i] = uint32_t(t);
-            carry = t >> 32;
-        }
-        int top = -1;
-        for (int i = kExactDigits - 1; i >= 0 && top < 0; --i)
-            if (dig[i]) top = i * 32 + 31 - __builtin_clz(dig[i]);
-        float r = 0.0f;
-        if (top >= 0) {
-            int lsb = top - 23;
-            if (lsb < kExactShift - 149) lsb = kExactShift - 149;     // fp32 subnormal spacing
-            auto bit = [&](int i) -> uint32_t { return (dig[i >> 5] >> (i & 31)) & 1u; };
-            uint64_t mant = 0;
-            for (int i = top; i >= lsb; --i) mant = (mant << 1) | bit(i);
-            const uint32_t round = lsb >= 1 ? bit(lsb - 1) : 0u;
-            uint32_t sticky = 0;
-            for (int i = lsb - 2; i >= 0 && !sticky; --i) sticky = bit(i);
-            if (round && (sticky || (mant & 1u))) mant += 1;
-            const double v = __builtin_ldexp(double(mant), lsb - kExactShift);   // exact
-            r = v > double(FLT_MAX) ? __builtin_inff() : float(v);
-        }
-        *result = r;
+}
+
+// The exact sum held in the digit array (digit i weighs 2^(32 i - 266);
+// carries not yet propagated), rounded to fp32 by hand: to nearest, ties to
+// even, subnormal spacing below 2^-126, infinity above the largest finite
+// value.  Called by one thread.
+__device__ float round_exact_digits(const unsigned long long *acc)
+{
+    uint32_t dig[kExactDigits];
+    uint64_t carry = 0;
+    for (int i = 0; i < kExactDigits; ++i) {
+        const uint64_t t = acc[i] + carry;
+        dig[i] = uint32_t(t);
+        carry = t >> 32;
     }
+    int top = -1;
+    for (int i = kExactDigits - 1; i >= 0 && top < 0; --i)
+        if (dig[i]) top = i * 32 + 31 - __builtin_clz(dig[i]);
+    float r = 0.0f;
+    if (top >= 0) {
+        int lsb = top - 23;
+        if (lsb < kExactShift - 149) lsb = kExactShift - 149;     // fp32 subnormal spacing
+        auto bit = [&](int i) -> uint32_t { return (dig[i >> 5] >> (i & 31)) & 1u; };
+        uint64_t mant = 0;
+        for (int i = top; i >= lsb; --i) mant = (mant << 1) | bit(i);
+        const uint32_t round = lsb >= 1 ? bit(lsb - 1) : 0u;
+        uint32_t sticky = 0;
+        for (int i = lsb - 2; i >= 0 && !sticky; --i) sticky = bit(i);
+        if (round && (sticky || (mant & 1u))) mant += 1;
+        const double v = __builtin_ldexp(double(mant), lsb - kExactShift);   // exact
+        r = v > double(FLT_MAX) ? __builtin_inff() : float(v);
+    }
+    return r;
+}
+
+// Exact sum of squares of the row, rounded to fp32 by hand: integer digits
+// in LDS (64-bit atomic adds of 32-bit pieces, carries resolved at the end by
+// one thread).  Called by every thread of the workgroup.
+__device__ float exact_sum_squares(const u32x4 (&w)[kNormU], unsigned long long *acc, float *result)
+{
+    if (threadIdx.x < kExactDigits) acc[threadIdx.x] = 0ull;
+    __syncthreads();
+    add_squares_exact<kNormU>(w, acc);
+    __syncthreads();
+    if (threadIdx.x == 0) *result = round_exact_digits(acc);
     __syncthreads();
     return *result;
 }
@@ -332,51 +349,10 @@ __device__ float exact_sum_squares_wave(const u32x4 (&xs)[NS], unsigned long lon
 {
     if (lane < kExactDigits) acc[lane] = 0ull;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-    for (int k = 0; k < NS; ++k) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t b = (xs[k][i / 2] >> (16 * (i % 2))) & 0x7FFFu;
-            const uint32_t e = b >> 7, m = b & 0x7Fu;
-            if (b != 0u) {
-                const int kexp = e ? int(e) - 134 : -133;
-                const uint32_t M = e ? (m | 0x80u) : m;
-                const int pos = 2 * kexp + kExactShift;
-                const uint64_t v = uint64_t(M * M) << (pos & 31);
-                atomicAdd(&acc[pos >> 5], (unsigned long long)(v & 0xFFFFFFFFull));
-                atomicAdd(&acc[(pos >> 5) + 1], (unsigned long long)(v >> 32));
-            }
-        }
-    }
+    add_squares_exact<NS>(xs, acc);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     uint32_t result = 0;
-    if (lane == 0) {
-        uint32_t dig[kExactDigits];
-        uint64_t carry = 0;
-        for (int i = 0; i < kExactDigits; ++i) {
-            const uint64_t t = acc[i] + carry;
-            dig[i] = uint32_t(t);
-            carry = t >> 32;
-        }
-        int top = -1;
-        for (int i = kExactDigits - 1; i >= 0 && top < 0; --i)
-            if (dig[i]) top = i * 32 + 31 - __builtin_clz(dig[i]);
-        float r = 0.0f;
-        if (top >= 0) {
-            int lsb = top - 23;
-            if (lsb < kExactShift - 149) lsb = kExactShift - 149;
-            auto bit = [&](int i) -> uint32_t { return (dig[i >> 5] >> (i & 31)) & 1u; };
-            uint64_t mant = 0;
-            for (int i = top; i >= lsb; --i) mant = (mant << 1) | bit(i);
-            const uint32_t round = lsb >= 1 ? bit(lsb - 1) : 0u;
-            uint32_t sticky = 0;
-            for (int i = lsb - 2; i >= 0 && !sticky; --i) sticky = bit(i);
-            if (round && (sticky || (mant & 1u))) mant += 1;
-            const double v = __builtin_ldexp(double(mant), lsb - kExactShift);
-            r = v > double(FLT_MAX) ? __builtin_inff() : float(v);
-        }
-        result = __float_as_uint(r);
-    }
+    if (lane == 0) result = __float_as_uint(round_exact_digits(acc));
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     return __uint_as_float(__builtin_amdgcn_readfirstlane(result));
 }
