@@ -18,13 +18,17 @@
 //   1. channel_amax_kernel: workgroups own (row chunk, 512-column stripe)
 //      tiles and write the chunk's column maxima (bf16 magnitude bits) to a
 //      caller-provided workspace [chunks, cols];
-//   2. channel_cast_kernel: each workgroup first reduces the chunk maxima of
-//      its stripe (all chunk loads in flight at once, then an LDS max across
+//   2. above 64 MiB of x, channel_scale_kernel (one workgroup per stripe)
+//      reduces the chunk maxima to the column scales, writes them to the
+//      output and to the workspace, and channel_rows_kernel converts one
+//      whole row per workgroup in the row-form cast's shape, its lanes
+//      reading their columns' scales from the workspace; the last rows go
+//      first, since the rows the first pass read last are the likeliest still
+//      in the 256 MB Infinity Cache.  Up to 64 MiB, channel_cast_kernel does
+//      both in one launch: each workgroup reduces the chunk maxima of its
+//      stripe (all chunk loads in flight at once, then an LDS max across
 //      waves) to the stripe's scales, which one workgroup per stripe also
-//      writes to the output; then it converts its rows against them.  Its
-//      workgroups take the row chunks in reverse order, so the rows the first
-//      pass read last, the ones most likely still in the 256 MB Infinity
-//      Cache, are read first.
+//      writes to the output, then converts its (chunk, stripe) tile.
 
 #include <hip/hip_runtime.h>
 
@@ -152,6 +156,8 @@ struct ChannelParams {
     void *s;
     uint16_t *ws;          // [chunks, cols] bf16 magnitude bits
     int64_t chunk_rows, chunks;
+    uint8_t *col_scales;   // per column: the biased exponent byte (power-of-two scales) or the fp32 scale
+    int32_t xcd_log2;      // xcd_order run length over the row-form pass's workgroups
 };
 
 // Rows [c0, c1) of one 512-column stripe, visited by the waves of a workgroup
@@ -346,6 +352,132 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(Chann
     }
 }
 
+// Column scales (between the two passes): one workgroup per 512-column
+// stripe reduces the stripe's chunk maxima (each wave its share of the
+// chunks, all loads in flight, then the LDS max across waves), writes the
+// scales to `s` and, for the row-form cast pass, to col_scales: the biased
+// exponent byte of each column's power-of-two scale, or its fp32 scale.
+template <int QD, bool POW2, int SF>
+__global__ __launch_bounds__(kWave * kChannelWPB) void channel_scale_kernel(ChannelParams p)
+{
+    __shared__ u32x4 part[kChannelWPB][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t cols = uint32_t(p.cols);
+    const uint32_t col = blockIdx.x * uint32_t(kSegCols) + uint32_t(lane) * 8u;
+    constexpr int kChunkLoads = int(kChannelMaxChunks) / kChannelWPB;
+    u32x4 cw[kChunkLoads];
+#pragma unroll
+    for (int k = 0; k < kChunkLoads; ++k) {
+        const int64_t c = wave + int64_t(k) * kChannelWPB;
+        cw[k] = u32x4{0u, 0u, 0u, 0u};
+        if (c < p.chunks) cw[k] = load16(row_buffer(p.ws + c * p.cols, cols * 2u), col * 2u);
+    }
+    u16x2 mx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx[j] = u16x2{0, 0};
+#pragma unroll
+    for (int k = 0; k < kChunkLoads; ++k) max_bf16x8(mx, cw[k]);
+    workgroup_max(mx, part, wave, lane);
+    if (wave != 0) return;
+    float sv[8];
+    uint32_t e8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t amax_bits = uint32_t((i & 1) ? mx[i / 2].y : mx[i / 2].x) << 16;
+        const Scale<QD, POW2> sc = group_scale<QD, POW2>(amax_bits);
+        sv[i] = sc.s;
+        e8[i] = sc.e8;
+    }
+    u32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = __float_as_uint(sv[i]);
+        b[i] = __float_as_uint(sv[4 + i]);
+    }
+    const u32x2 bytes{e8[0] | (e8[1] << 8) | (e8[2] << 16) | (e8[3] << 24),
+                      e8[4] | (e8[5] << 8) | (e8[6] << 16) | (e8[7] << 24)};
+    if constexpr (SF == kScaleF32) {
+        const __amdgpu_buffer_rsrc_t srow = row_buffer(p.s, cols * 4u);
+        __builtin_amdgcn_raw_buffer_store_b128(a, srow, int(col * 4u), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(b, srow, int(col * 4u + 16u), 0, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b64(bytes, row_buffer(p.s, cols), int(col), 0, 0);
+    }
+    if constexpr (POW2) {
+        __builtin_amdgcn_raw_buffer_store_b64(bytes, row_buffer(p.col_scales, cols), int(col), 0, 0);
+    } else {
+        const __amdgpu_buffer_rsrc_t crow = row_buffer(p.col_scales, cols * 4u);
+        __builtin_amdgcn_raw_buffer_store_b128(a, crow, int(col * 4u), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(b, crow, int(col * 4u + 16u), 0, 0);
+    }
+}
+
+// Pass 2 in row form (x above 64 MiB): a workgroup converts one whole row,
+// wave w taking the runs of two 512-column segments w, w + W, ... (one run
+// per wave up to 16384 columns) with its lanes' 16 column scales read from
+// the workspace.  Workgroups in XCD order, last rows first (the rows the
+// first pass read last are the likeliest still cached).  Measured on MI355X
+// against the (chunk, stripe) tile form: -2.1 % at 32768 x 7168, -1.5 % at
+// 16384, -1.2 % at 8192, +3.7 % at 4096 (x of 56 MiB keeps the tile form).
+template <int QD, bool POW2, int SF, int POL>
+__global__ __launch_bounds__(1024) void channel_rows_kernel(ChannelParams p)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = int(blockDim.x) >> 6;
+    const uint32_t cols = uint32_t(p.cols);
+    const uint32_t qbytes = QD == kE4M3 ? cols : cols / 2;
+    const int runs = int((cols + 2 * kSegCols - 1) / (2 * kSegCols));
+    for (int64_t i = blockIdx.x; i < p.rows; i += gridDim.x) {
+        const int64_t row = p.rows - 1 - xcd_order(i, p.rows, p.xcd_log2);
+        const __amdgpu_buffer_rsrc_t xrow = row_buffer(p.x + row * p.x_ld, cols * 2u);
+        const __amdgpu_buffer_rsrc_t qrow = row_buffer(p.q + row * p.q_ld, qbytes);
+        for (int run = wave; run < runs; run += nw) {
+            const uint32_t col0 = uint32_t(run) * 2u * kSegCols + uint32_t(lane) * 8u;
+            u32x4 w[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                w[k] = __builtin_amdgcn_raw_buffer_load_b128(xrow, int((col0 + k * kSegCols) * 2u), 0, POL);
+            // the lane's column scales: 2^-e from the exponent bytes, or s
+            float sc[2][8];
+            if constexpr (POW2) {
+                const __amdgpu_buffer_rsrc_t crow = row_buffer(p.col_scales, cols);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(crow, int(col0 + k * kSegCols), 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        sc[k][i] = __uint_as_float((254u - ((e[i / 4] >> (8 * (i % 4))) & 0xFFu)) << 23);
+                }
+            } else {
+                const __amdgpu_buffer_rsrc_t crow = row_buffer(p.col_scales, cols * 4u);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const u32x4 a = load16(crow, (col0 + k * kSegCols) * 4u);
+                    const u32x4 b = load16(crow, (col0 + k * kSegCols) * 4u + 16u);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sc[k][i] = __uint_as_float(a[i]);
+                        sc[k][4 + i] = __uint_as_float(b[i]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                float x[8], v[8];
+                widen8(w[k], x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = scaled<QD, POW2, kApplyMul>(x[i], sc[k][i], sc[k][i]);
+                const u32x2 codes = encode8<QD>(v);
+                const uint32_t col = col0 + k * kSegCols;
+                if constexpr (QD == kE4M3) store8(qrow, col, codes);
+                else store4(qrow, col / 2, codes.x);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 
@@ -356,7 +488,9 @@ struct BlockTable {
     BlockFn fn[3][4][2][3];      // [rows per wave 4/8/16][block_cols index][code format][variant]
 };
 struct ChannelTable {
-    ChannelFn cast[2][3][3];     // [code format][variant][x above 128 MiB, up to 128 MiB, up to 64 MiB]
+    ChannelFn cast[2][3];        // [code format][variant]: x up to 64 MiB
+    ChannelFn scale[2][3];       // [code format][variant]: above 64 MiB, then
+    ChannelFn rows[2][3][2];     //   [code format][variant][x above 128 MiB (non-temporal loads), up to 128 MiB]
 };
 
 template <int BC, int QD, int RPW>
@@ -396,21 +530,21 @@ int block_rpw_index(int64_t block_rows, int64_t tiles, int cus)
     return block_rows > 32 ? 1 : 0;
 }
 
-template <int QD, int PI, int POL>
-void fill_channel_policy(ChannelTable &t)
-{
-    constexpr int U = PI == 2 ? kChannelSmallUnroll : kChannelUnroll;
-    t.cast[QD][0][PI] = channel_cast_kernel<QD, false, kScaleF32, POL, U>;
-    t.cast[QD][1][PI] = channel_cast_kernel<QD, true, kScaleF32, POL, U>;
-    t.cast[QD][2][PI] = channel_cast_kernel<QD, true, kScaleUE8M0, POL, U>;
-}
-
 template <int QD>
 void fill_channel(ChannelTable &t)
 {
-    fill_channel_policy<QD, 0, kNonTemporal>(t);
-    fill_channel_policy<QD, 1, 0>(t);
-    fill_channel_policy<QD, 2, 0>(t);
+    t.cast[QD][0] = channel_cast_kernel<QD, false, kScaleF32, 0, kChannelSmallUnroll>;
+    t.cast[QD][1] = channel_cast_kernel<QD, true, kScaleF32, 0, kChannelSmallUnroll>;
+    t.cast[QD][2] = channel_cast_kernel<QD, true, kScaleUE8M0, 0, kChannelSmallUnroll>;
+    t.scale[QD][0] = channel_scale_kernel<QD, false, kScaleF32>;
+    t.scale[QD][1] = channel_scale_kernel<QD, true, kScaleF32>;
+    t.scale[QD][2] = channel_scale_kernel<QD, true, kScaleUE8M0>;
+    t.rows[QD][0][0] = channel_rows_kernel<QD, false, kScaleF32, kNonTemporal>;
+    t.rows[QD][1][0] = channel_rows_kernel<QD, true, kScaleF32, kNonTemporal>;
+    t.rows[QD][2][0] = channel_rows_kernel<QD, true, kScaleUE8M0, kNonTemporal>;
+    t.rows[QD][0][1] = channel_rows_kernel<QD, false, kScaleF32, 0>;
+    t.rows[QD][1][1] = channel_rows_kernel<QD, true, kScaleF32, 0>;
+    t.rows[QD][2][1] = channel_rows_kernel<QD, true, kScaleUE8M0, 0>;
 }
 
 ChannelTable make_channel_table()
@@ -448,7 +582,7 @@ tk_status validate_common(const void *x, int64_t rows, int64_t cols, int64_t x_l
 // it passes the device address that hipGetSymbolAddress gives, looked up once
 // per device with that device current.  Every no-allocation call on a GPU
 // shares that GPU's copy.
-constexpr int64_t kNoAllocScratchBytes = int64_t(1) << 20;
+constexpr int64_t kNoAllocScratchBytes = int64_t(1088) << 10;   // 32 chunks x 16384 columns x 2 B + 4 B per column
 
 }  // namespace
 
@@ -490,6 +624,11 @@ int64_t channel_chunks(int64_t rows)
     return (rows + cr - 1) / cr;
 }
 
+// Workspace: the chunk maxima [chunks, cols] (bf16 bits), then from the next
+// 256-byte boundary the column scales (4 bytes per column at most).
+int64_t channel_maxima_bytes(int64_t rows, int64_t cols) { return (channel_chunks(rows) * cols * 2 + 255) / 256 * 256; }
+int64_t channel_workspace_bytes(int64_t rows, int64_t cols) { return channel_maxima_bytes(rows, cols) + cols * 4; }
+
 // The two passes of the per-channel cast on an argument-checked call, with
 // `workspace` (device memory of at least tk_per_channel_workspace_bytes).
 tk_status launch_channel(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void *q, int64_t q_ld, void *scales,
@@ -501,23 +640,38 @@ tk_status launch_channel(const void *x, int64_t rows, int64_t cols, int64_t x_ld
     const int64_t stripes = (cols + kSegCols - 1) / kSegCols;
     const int64_t tiles = chunks * stripes;
     if (tiles > int64_t(0x7FFFFFFF)) return TK_ERROR_UNSUPPORTED;
+    const int64_t row_blocks = rows < int64_t(0x7FFFFFFF) ? rows : int64_t(0x7FFFFFFF);   // taller inputs loop
     ChannelParams p{static_cast<const uint16_t *>(x), rows, cols, x_ld, static_cast<uint8_t *>(q), q_ld, scales,
-                    static_cast<uint16_t *>(workspace), chunk_rows, chunks};
+                    static_cast<uint16_t *>(workspace), chunk_rows, chunks,
+                    static_cast<uint8_t *>(workspace) + channel_maxima_bytes(rows, cols),
+                    xcd_run_log2(rows, row_blocks, cols * 2)};
     void *args[] = {&p};
-    // Size classes of x.  Up to half the 256 MiB Infinity Cache the second
-    // pass uses ordinary loads (with inputs rotated over three buffer sets:
-    // -6 % at 4096 x 7168; at 16384 x 7168, 235 MB, ordinary loads were 4 %
-    // slower), non-temporal ones beyond; up to 64 MiB both passes keep 2 rows
-    // in flight per wave instead of 4 (-10 % at 4096 x 7168; 1 % slower at
-    // 8192 rows, 2-5 % at 16384 and 32768).
+    // Size classes of x.  Up to 64 MiB: both passes keep 2 rows in flight
+    // per wave instead of 4 (-10 % at 4096 x 7168; 1 % slower at 8192 rows,
+    // 2-5 % at 16384 and 32768), and the second pass is the tile form with
+    // ordinary loads.  Above: the scale kernel and the row form, whose loads
+    // are ordinary up to half the 256 MiB Infinity Cache and non-temporal
+    // beyond (ordinary: +5 % at 16384 x 7168, +6 % at 32768).
     const int64_t x_bytes = rows * cols * 2;
-    const int pi = x_bytes <= kChannelSmallBytes ? 2 : x_bytes <= kChannelCachedBytes ? 1 : 0;
-    const void *amax_fn = pi == 2 ? reinterpret_cast<const void *>(channel_amax_kernel<kChannelSmallUnroll>)
-                                  : reinterpret_cast<const void *>(channel_amax_kernel<kChannelUnroll>);
+    const bool small = x_bytes <= kChannelSmallBytes;
+    const void *amax_fn = small ? reinterpret_cast<const void *>(channel_amax_kernel<kChannelSmallUnroll>)
+                                : reinterpret_cast<const void *>(channel_amax_kernel<kChannelUnroll>);
     if (hipLaunchKernel(amax_fn, dim3(uint32_t(tiles)), dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
         return TK_ERROR_LAUNCH;
-    if (hipLaunchKernel(reinterpret_cast<const void *>(table.cast[out_dtype][variant][pi]), dim3(uint32_t(tiles)),
+    if (small) {
+        if (hipLaunchKernel(reinterpret_cast<const void *>(table.cast[out_dtype][variant]), dim3(uint32_t(tiles)),
+                            dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
+            return TK_ERROR_LAUNCH;
+        return TK_SUCCESS;
+    }
+    const int64_t runs = (cols + 2 * kSegCols - 1) / (2 * kSegCols);
+    const int waves = int(runs < 16 ? runs : 16);
+    if (hipLaunchKernel(reinterpret_cast<const void *>(table.scale[out_dtype][variant]), dim3(uint32_t(stripes)),
                         dim3(kWave * kChannelWPB), args, 0, s) != hipSuccess)
+        return TK_ERROR_LAUNCH;
+    const int pol = x_bytes <= kChannelCachedBytes ? 1 : 0;
+    if (hipLaunchKernel(reinterpret_cast<const void *>(table.rows[out_dtype][variant][pol]), dim3(uint32_t(row_blocks)),
+                        dim3(kWave * waves), args, 0, s) != hipSuccess)
         return TK_ERROR_LAUNCH;
     return TK_SUCCESS;
 }
@@ -573,7 +727,7 @@ tk_status tk_per_block_cast(const void *x, int64_t rows, int64_t cols, int64_t x
 int64_t tk_per_channel_workspace_bytes(int64_t rows, int64_t cols)
 {
     if (rows <= 0 || cols <= 0) return 0;
-    return channel_chunks(rows) * cols * 2;
+    return channel_workspace_bytes(rows, cols);
 }
 
 tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void *q, int64_t q_ld,

@@ -208,9 +208,11 @@ tk_status tk_per_block_cast(const void *x, int64_t rows, int64_t cols, int64_t x
  *            tk_per_channel_workspace_bytes(rows, cols) bytes; its contents
  *            on entry do not matter and are undefined afterwards.  Calls that
  *            share a workspace must be ordered on one stream.
- * The cast reads x twice (column maxima, then the codes) in two kernels on
- * `stream`.  Errors as for tk_per_token_cast; a missing or short workspace
- * is TK_ERROR_INVALID_VALUE.
+ * The cast reads x twice (column maxima, then the codes), all on `stream`:
+ * two kernels up to 64 MiB of x, three above (the column scales computed
+ * between the two passes).  The workspace holds the column maxima of up to
+ * 32 row chunks and then the column scales.  Errors as for tk_per_token_cast;
+ * a missing or short workspace is TK_ERROR_INVALID_VALUE.
  */
 int64_t tk_per_channel_workspace_bytes(int64_t rows, int64_t cols);
 tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
@@ -224,8 +226,9 @@ tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t
  * capture, tight serving loops, harnesses that forbid allocation).  Same
  * arguments, kernels and results as tk_per_channel_cast without the workspace
  * pair: the column maxima go to the library's own static device array of
- * tk_per_channel_noalloc_max_workspace_bytes() bytes (1 MiB: 32 chunks of
- * cols <= 16384 columns), one per GPU, held until the process ends.  The call
+ * tk_per_channel_noalloc_max_workspace_bytes() bytes (1088 KiB: the maxima
+ * of 32 row chunks and the scales of up to 16384 columns), one per GPU, held
+ * until the process ends.  The call
  * itself allocates nothing.  Inputs that need more than that
  * (tk_per_channel_workspace_bytes(rows, cols) above the maximum) return
  * TK_ERROR_UNSUPPORTED with nothing launched.  Every call on a GPU shares that

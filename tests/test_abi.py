@@ -202,7 +202,7 @@ def test_per_channel_validation(kw, want):
     (dict(cols=12), INVALID), (dict(cols=0), INVALID), (dict(rows=-1), INVALID), (dict(out_dtype=2), INVALID),
     (dict(scale_fmt=1, round_pow2=0), INVALID), (dict(x_ld=100), INVALID), (dict(x=0), INVALID), (dict(s=0), INVALID),
     (dict(x=X + 8), MISALIGNED), (dict(s=S + 8), MISALIGNED),
-    (dict(rows=4096, cols=16392, x_ld=16392, q_ld=16392), UNSUPPORTED),    # column maxima above 1 MiB
+    (dict(rows=4096, cols=16392, x_ld=16392, q_ld=16392), UNSUPPORTED),    # workspace above 1088 KiB
     (dict(rows=0, x=0, q=0, s=0), 0),
 ])
 def test_per_channel_noalloc_validation(kw, want):
@@ -212,17 +212,26 @@ def test_per_channel_noalloc_validation(kw, want):
     a.update(kw)
     assert binding.tk_per_channel_cast_noalloc(a["x"], a["rows"], a["cols"], a["x_ld"], a["q"], a["q_ld"], a["s"],
                                                a["out_dtype"], a["round_pow2"], a["scale_fmt"], 0) == want
-    assert binding.tk_per_channel_noalloc_max_workspace_bytes() == 1 << 20
+    assert binding.tk_per_channel_noalloc_max_workspace_bytes() == 1088 << 10
+
+
+def _ws(chunks, cols):
+    """Chunk maxima (2 bytes per column and chunk) padded to 256 bytes, then
+    4 bytes of scale per column."""
+    return (chunks * cols * 2 + 255) // 256 * 256 + cols * 4
 
 
 def test_per_channel_workspace_size():
     assert tk.tk_per_channel_workspace_bytes(0, 256) == 0
-    assert tk.tk_per_channel_workspace_bytes(1, 256) == 256 * 2
+    assert tk.tk_per_channel_workspace_bytes(1, 256) == _ws(1, 256)
     # at most 32 chunks of at least 64 rows
-    assert tk.tk_per_channel_workspace_bytes(64, 256) == 256 * 2
-    assert tk.tk_per_channel_workspace_bytes(65, 256) == 2 * 256 * 2
-    assert tk.tk_per_channel_workspace_bytes(4096, 7168) == 32 * 7168 * 2
-    assert tk.tk_per_channel_workspace_bytes(10**6, 16) <= 32 * 16 * 2
+    assert tk.tk_per_channel_workspace_bytes(64, 256) == _ws(1, 256)
+    assert tk.tk_per_channel_workspace_bytes(65, 256) == _ws(2, 256)
+    assert tk.tk_per_channel_workspace_bytes(4096, 7168) == _ws(32, 7168)
+    assert tk.tk_per_channel_workspace_bytes(70, 8) == 256 + 32            # the maxima padded to 256 bytes
+    assert tk.tk_per_channel_workspace_bytes(10**6, 16) <= _ws(32, 16)
+    # the largest input the allocation-free entry point takes: 32 chunks of 16384 columns
+    assert tk.tk_per_channel_workspace_bytes(4096, 16384) == binding.tk_per_channel_noalloc_max_workspace_bytes()
 
 
 @pytest.mark.parametrize("kw,want", [

@@ -165,6 +165,18 @@ def test_per_channel_size_classes(rows):
     check_channel(x, "e4m3", True, "ue8m0", label="size classes")
 
 
+@pytest.mark.parametrize("rows,cols,dt,p2,sf", [(4100, 8200, "e2m1", True, "f32"), (4100, 8200, "e4m3", False, "f32"),
+                                                 (2100, 16392, "e4m3", True, "ue8m0")])
+def test_per_channel_row_form_ragged(rows, cols, dt, p2, sf):
+    """Above 64 MiB of x the codes come from the row-form pass: rows whose
+    width is not a whole number of 1024-column runs, and rows of more runs
+    than a workgroup has waves (16392 columns: 17 runs), with ragged row
+    counts in the workgroup order."""
+    assert rows * cols * 2 > 64 << 20
+    x = inputs.generate_small(rows + cols, rows, cols, "student_t3")
+    check_channel(x, dt, p2, sf, x_ld=cols + 8, label="row form")
+
+
 def test_per_channel_zero_columns_and_reused_workspace():
     """Columns of zeros take the floored scale; one workspace serves a larger
     and then a smaller call (its contents on entry do not matter)."""

@@ -68,8 +68,8 @@ def test_noalloc_size_limit():
     """A cast whose column maxima exceed the static workspace is refused
     before anything is launched; the largest that fits runs."""
     limit = binding.tk_per_channel_noalloc_max_workspace_bytes()
-    assert limit == 1 << 20
-    rows, cols = 4096, 16384 + 8                 # 32 chunks x 16392 columns x 2 bytes > 1 MiB
+    assert limit == 1088 << 10
+    rows, cols = 4096, 16384 + 8                 # 32 chunks x 16392 columns x 2 bytes + 4 per column > 1088 KiB
     assert tk.tk_per_channel_workspace_bytes(rows, cols) > limit
     log(f"[gpu] per-channel no-alloc refused at rows={rows} cols={cols}")
     x = torch.zeros((rows, cols), dtype=torch.bfloat16, device="cuda")
