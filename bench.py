@@ -104,6 +104,39 @@ def summarize_pmc(workload_index, fetch_csv, write_csv, traffic_file=None):
     return entry
 
 
+# Raw TCC/EA request counters, the independent check of the calibrated
+# FETCH_SIZE figure: FETCH_SIZE prices every read request that is neither a
+# 32-byte one nor counted by TCC_BUBBLE at 64 bytes, and on this GPU the
+# streaming reads are 128-byte requests that TCC_BUBBLE does not count.
+EA_READ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum", "TCC_EA0_RDREQ_DRAM_sum")
+EA_WRITE_COUNTERS = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_DRAM_sum")
+
+
+def summarize_ea(read_csv, write_csv, read_request_bytes=128):
+    """Per kernel: the median request counts of two rocprofv3 --pmc runs
+    (EA_READ_COUNTERS, EA_WRITE_COUNTERS) and the bytes they stand for: reads
+    at 32 bytes for a 32-byte request and `read_request_bytes` for any other,
+    writes at 64 bytes for a 64-byte request and 32 for any other.  The
+    library's 1 GiB streaming copy, run in the same processes, checks the
+    request size: its bytes must come out at 1 GiB each way."""
+    import numpy as np
+    out = {}
+    for path, counters in ((read_csv, EA_READ_COUNTERS), (write_csv, EA_WRITE_COUNTERS)):
+        for c in counters:
+            for k, v in _pmc_per_kernel(path, c).items():
+                out.setdefault(k, {})[c] = float(np.median(v))
+    for k, d in out.items():
+        if "TCC_EA0_RDREQ_sum" in d:
+            r32 = d.get("TCC_EA0_RDREQ_32B_sum", 0.0)
+            d["read_bytes"] = int(round(32 * r32 + read_request_bytes * (d["TCC_EA0_RDREQ_sum"] - r32)))
+        if "TCC_EA0_WRREQ_sum" in d:
+            w64 = d.get("TCC_EA0_WRREQ_64B_sum", 0.0)
+            d["write_bytes"] = int(round(64 * w64 + 32 * (d["TCC_EA0_WRREQ_sum"] - w64)))
+    for k, d in sorted(out.items()):
+        print(f"{k[:100]:100s} " + " ".join(f"{c}={v:.0f}" for c, v in d.items()))
+    return out
+
+
 def _oracle_step(op: str, w, block, weight_bits):
     """(fn(rows of x) -> None, rows must be a multiple of, algorithmic bytes per row)
     for one operation's CPU oracle; the per-row byte count matches the bench's."""
@@ -260,10 +293,15 @@ def main():
                     help="also run 3 device-to-device copies of 1 GiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json")
+    ap.add_argument("--summarize-ea", nargs=2, metavar=("READ_CSV", "WRITE_CSV"),
+                    help="per-kernel TCC/EA request counts and bytes from two rocprofv3 --pmc runs")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         summarize_pmc(args.workload, *args.summarize_pmc)
+        return
+    if args.summarize_ea:
+        summarize_ea(*args.summarize_ea)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

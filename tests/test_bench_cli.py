@@ -1,6 +1,7 @@
 """bench.py's command line on the CPU: it measures one GPU and refuses more."""
 from __future__ import annotations
 
+import csv
 import os
 import pathlib
 import subprocess
@@ -58,3 +59,34 @@ def test_counter_summary_scales_by_the_calibration_copy(tmp_path):
     assert entry["kernel_source_sha256_16"] == bench.kernel_source_hash()
     import json
     assert json.loads((tmp_path / "t.json").read_text())["workload4"] == entry
+
+
+def test_ea_request_summary(tmp_path):
+    """Read bytes = 32 per 32-byte request + 128 per other request, write bytes
+    = 64 per 64-byte request + 32 per other; medians over dispatches, a
+    dispatch's rows summed."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    copy = "(anonymous namespace)::copy_stream_kernel(...)"
+    cast = "void (anonymous namespace)::cast_rows_kernel<32, 1, true, 1, 2>(...)"
+    rd, wr = tmp_path / "rd.csv", tmp_path / "wr.csv"
+    with open(rd, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, k, c, v in [(1, copy, "TCC_EA0_RDREQ_sum", 1 << 23), (1, copy, "TCC_EA0_RDREQ_32B_sum", 0),
+                           (2, cast, "TCC_EA0_RDREQ_sum", 60), (2, cast, "TCC_EA0_RDREQ_sum", 40),
+                           (2, cast, "TCC_EA0_RDREQ_32B_sum", 10), (3, cast, "TCC_EA0_RDREQ_sum", 100),
+                           (3, cast, "TCC_EA0_RDREQ_32B_sum", 10), (4, cast, "TCC_EA0_RDREQ_sum", 300),
+                           (4, cast, "TCC_EA0_RDREQ_32B_sum", 10)]:
+            w.writerow([d, k, c, v])
+    with open(wr, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, k, c, v in [(1, copy, "TCC_EA0_WRREQ_sum", 1 << 24), (1, copy, "TCC_EA0_WRREQ_64B_sum", 1 << 24),
+                           (2, cast, "TCC_EA0_WRREQ_sum", 50), (2, cast, "TCC_EA0_WRREQ_64B_sum", 40)]:
+            w.writerow([d, k, c, v])
+    out = bench.summarize_ea(rd, wr)
+    assert out[copy]["read_bytes"] == 1 << 30 and out[copy]["write_bytes"] == 1 << 30
+    assert out[cast]["TCC_EA0_RDREQ_sum"] == 100                         # median of 100, 100, 300
+    assert out[cast]["read_bytes"] == 32 * 10 + 128 * 90
+    assert out[cast]["write_bytes"] == 64 * 40 + 32 * 10
