@@ -132,10 +132,6 @@ __global__ __launch_bounds__(kWave * kMaxBlockWaves) void block_cast_kernel(Bloc
 constexpr int kChannelWPB = TK_CHANNEL_WPB;        // waves per workgroup
 constexpr int kChannelUnroll = TK_CHANNEL_UNROLL;  // rows in flight per wave
 constexpr int kChannelSmallUnroll = 2;             // the same for x of at most kChannelSmallBytes
-#ifndef TK_CHANNEL_REVERSE
-#define TK_CHANNEL_REVERSE 0
-#endif
-constexpr bool kChannelReverse = TK_CHANNEL_REVERSE != 0;
 // The first pass reads x with ordinary (allocating) loads, so that as much of
 // x as the caches hold is still there for the second pass.
 #ifndef TK_CHANNEL_P1_POLICY
@@ -257,11 +253,12 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_amax_kernel(Chann
     }
 }
 
-// Pass 2: the stripe's scales from the chunk maxima, then codes against the
-// column scales.  The first batch of rows is loaded before the chunk maxima
-// are reduced, so their latencies overlap.  P2_POLICY: the loads' cache
-// policy (ordinary when x is small enough to stay in the Infinity Cache,
-// where the first pass left it; non-temporal otherwise).
+// Pass 2 for x of up to 64 MiB: the stripe's scales from the chunk maxima,
+// then codes against the column scales, the chunks taken last first (the
+// rows the first pass read last are the likeliest still cached).  The first
+// batch of rows is loaded before the chunk maxima are reduced, so their
+// latencies overlap.  P2_POLICY: the loads' cache policy (ordinary: x of
+// this size stays in the Infinity Cache, where the first pass left it).
 template <int QD, bool POW2, int SF, int P2_POLICY, int U>
 __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(ChannelParams p)
 {
@@ -277,11 +274,8 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(Chann
     const uint32_t col = stripe * uint32_t(kSegCols) + uint32_t(lane) * 8u;
     const RowBatches<U, P2_POLICY> rb{p.x, p.x_ld, c0, c1, cols * 2u, col * 2u, wave};
     const int64_t nb = rb.batches();
-    // Batch order: descending when kChannelReverse, so that the rows the
-    // first pass read last (the likeliest still cached) come first.
-    auto batch_at = [&](int64_t i) { return kChannelReverse ? nb - 1 - i : i; };
     u32x4 w[U];
-    rb.load(batch_at(0), w);
+    rb.load(0, w);
 
     // Column maxima of this lane's 8 columns over every chunk: wave w takes
     // chunks w, w + W, ... (all its loads issued before any is used).
@@ -332,10 +326,10 @@ __global__ __launch_bounds__(kWave * kChannelWPB) void channel_cast_kernel(Chann
     const uint32_t qbytes = QD == kE4M3 ? cols : cols / 2;
     for (int64_t i = 0; i < nb; ++i) {
         u32x4 wn[U];
-        rb.load(batch_at(i + 1), wn);       // nothing past the last batch
+        rb.load(i + 1, wn);                 // nothing past the last batch
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const int64_t row = rb.row(batch_at(i), k);
+            const int64_t row = rb.row(i, k);
             if (row < c1) {
                 float x[8], v[8];
                 widen8(w[k], x);
