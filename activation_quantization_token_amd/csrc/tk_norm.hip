@@ -581,7 +581,9 @@ __global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void r
             const uint32_t col = uint32_t(k) * kSegCols + uint32_t(lane) * 8u;
             const Quantized qz = norm_segment<G, QD, POW2>(xs[k], r, lds_weight, col);
             codes[k] = qz.codes;
-            asm volatile("" : "+v"(codes[k].x), "+v"(codes[k].y));   // converted now, not at the store
+            // converted now, not at the store (E2M1 codes are one word)
+            if constexpr (QD == kE4M3) asm volatile("" : "+v"(codes[k].x), "+v"(codes[k].y));
+            else asm volatile("" : "+v"(codes[k].x));
             stage_scales<G, SF>(qz, col, cols, lane, stage[wave]);
         }
 #pragma unroll

@@ -366,15 +366,17 @@ __device__ __forceinline__ uint32_t piece_group_max(uint32_t v, int lane)
 }
 
 // 4 clamped values -> codes: E4M3 in 4 bytes, E2M1 in 4 nibbles of the low
-// 16 bits (value 2i in the low nibble of byte i).
+// 16 bits (value 2i in the low nibble of byte i; the high 16 bits are not
+// defined, and only the low half is stored).  As in encode8, the first
+// converter is given its own first input's bits as the word to write into.
 template <int QD>
 __device__ __forceinline__ uint32_t encode4(const float (&v)[4])
 {
     if constexpr (QD == kE4M3) {
-        const uint32_t lo = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false));
+        const uint32_t lo = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], __float_as_int(v[0]), false));
         return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], int(lo), true));
     } else {
-        const uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
+        const uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(v[0]), v[0], v[1], 1.0f, 0);
         return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], 1.0f, 1);
     }
 }

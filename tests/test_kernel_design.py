@@ -74,11 +74,23 @@ def _pow2_by_fields(a: np.ndarray, qd: str) -> np.ndarray:
     return e - 2 + (m > 0x400000)          # D = 3 * 2: round up past mantissa 1.5
 
 
+def _pow2_by_carry(a: np.ndarray, qd: str) -> np.ndarray:
+    """The one-addition form the fused RMSNorm cast uses: 2^23 - T - 1 added
+    to a's bits carries into the exponent field exactly when the significand
+    field passes T, and the same addition takes off the 8 (E4M3) or 2 (E2M1);
+    the mask keeps the exponent field."""
+    b = a.view(np.uint32).astype(np.uint64)
+    add = ((0x1FFFFF - (8 << 23)) if qd == "e4m3" else (0x3FFFFF - (2 << 23))) % (1 << 32)   # as a uint32
+    s_bits = ((b + np.uint64(add)) & 0xFFFFFFFF) & 0x7F800000
+    return (s_bits >> 23).astype(np.uint32)
+
+
 def test_pow2_scale_without_division():
     """fl32(a/448) and fl32(a/6) are powers of two only when the exact
     quotients are, so ceil(log2) of the rounded quotient follows from a's
-    fields: checked for every fp32 significand at exponents spanning the
-    floored range [1e-4, FLT_MAX], and at the floor itself."""
+    fields (compared, or by one carrying addition): checked for every fp32
+    significand at exponents spanning the floored range [1e-4, FLT_MAX], and
+    at the floor itself."""
     mant = np.arange(1 << 23, dtype=np.uint32)
     floor_bits = np.float32(1e-4).view(np.uint32)
     for field in (113, 114, 120, 127, 128, 150, 200, 253, 254):
@@ -90,3 +102,5 @@ def test_pow2_scale_without_division():
             want = _pow2_by_division(a, d)
             got = _pow2_by_fields(a, qd)
             assert np.array_equal(got, want), (field, qd, int(np.argmax(got != want)))
+            carry = _pow2_by_carry(a, qd)
+            assert np.array_equal(carry, want), (field, qd, int(np.argmax(carry != want)))
