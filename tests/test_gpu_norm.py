@@ -130,11 +130,11 @@ def _wave_rows():
     return torch.cuda.get_device_properties(0).multi_processor_count * 16
 
 
-def _looped_input(cols, seed):
-    """A tall input (2 x 4096 + 7 rows on 256 CUs) with exact-path rows placed
-    at its start, middle and end and around multiples of the row count of
-    16 waves per CU."""
-    n = _wave_rows()
+def _looped_input(cols, seed, n=None):
+    """A tall input (2 n + 7 rows; n = 4096 on 256 CUs, the row count of 16
+    waves per CU, by default) with exact-path rows placed at its start, middle
+    and end and around multiples of n."""
+    n = _wave_rows() if n is None else n
     rows = 2 * n + 7
     x = inputs.generate_small(seed, rows, cols, "student_t3")
     special = (np.stack(_ambiguous_rows(cols)).view(np.uint32) >> 16).astype(np.uint16)
@@ -159,6 +159,19 @@ def test_rmsnorm_cast_tall_inputs(dt, p2, sf, group):
 def test_rmsnorm_cast_tall_inputs_wide(cols, group, dt, p2, sf):
     x = _looped_input(cols, 5)
     check_norm_cast(x, _weight(1, cols), 1e-6, group, dt, p2, sf, label="tall")
+
+
+@pytest.mark.parametrize("cols", [9216, 16384])
+def test_rmsnorm_workgroup_kernel_loops_over_rows(cols):
+    """Rows wider than 7168 channels take the persistent workgroup-per-row
+    kernel, whose grid holds 32 waves per CU (cols / 1024 waves a workgroup)
+    and whose workgroups prefetch their next row: twice its grid of rows and
+    7 more, with exact-path rows at the grid's multiples."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = cus * max(1, 32 // (cols // 1024))
+    x = _looped_input(cols, 13, n=grid)
+    check_norm_cast(x, _weight(3, cols), 1e-6, 64, "e2m1", True, "ue8m0", label="workgroup kernel, tall")
+    check_norm(x, _weight(3, cols), 1e-6, "bf16", label="workgroup kernel, tall")
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
