@@ -25,6 +25,7 @@ ROOT = pathlib.Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, AMD published peak
+MALL_BYTES = 256 << 20           # MI355X Infinity Cache
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 # the per-token cast kernels' sources: their hash keys the stored counter runs
 KERNEL_SRCS = [ROOT / "activation_quantization_token_amd" / "csrc" / n for n in ("tk_quant.hip", "tk_device.h")]
@@ -286,9 +287,14 @@ def main():
                          "or RMSNorm fused with the workload's per-token cast")
     ap.add_argument("--block", default="128x128", help="block rows x block columns for --op per_block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sets", type=int, default=3, help="distinct input/output sets rotated over")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="distinct input/output sets rotated over (default: at least 3, and enough that the sets "
+                         "hold twice the 256 MB Infinity Cache)")
     ap.add_argument("--flushed", type=int, default=50,
                     help="extra launches timed one by one, each after a 512 MiB copy that flushes the caches")
+    ap.add_argument("--vendor-copy", action="store_true",
+                    help="also time the runtime's device-to-device copy and the library's streaming copy of "
+                         "half the step's bytes each way")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run 3 device-to-device copies of 1 GiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -320,9 +326,13 @@ def main():
     dev = torch.device("cuda:0")
     x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     # Rotate over distinct input/output sets so that no step can be served
-    # from the 256 MB Infinity Cache with data the previous step touched.
+    # from the 256 MB Infinity Cache with data an earlier step touched: the
+    # sets together hold at least twice the cache (with three sets of a
+    # ~89 MB workload, 267 MB, some of the oldest set's data was still cached:
+    # 3 % faster than with eight).
+    n_sets = args.sets if args.sets > 0 else max(3, -(-(2 * MALL_BYTES) // w.algorithmic_bytes()))
     sets = []
-    for i in range(args.sets):
+    for i in range(n_sets):
         xi = x0 if i == 0 else x0.clone()
         sets.append((xi, *tk.empty_outputs(w.rows, w.cols, w.group, w.out_dtype, w.scale_fmt, dev)))
     if args.op != "cast" and w.swiglu:
@@ -540,6 +550,44 @@ def main():
     ceil_us = c0.elapsed_time(c1) * 1e3 / args.steps
     del csrc, cdst
 
+    # The runtime's own device-to-device copy (hipMemcpyAsync through
+    # torch's copy_) against the library's streaming copy, each moving half
+    # the step's bytes each way, settled and timed like the operation: a check
+    # that the library's streams are no slower than the vendor's.
+    vendor = None
+    if args.vendor_copy:
+        half = (nbytes // 2) - (nbytes // 2) % 16
+        vsrc = [torch.ones(half, dtype=torch.uint8, device=dev) for _ in range(len(sets))]
+        vdst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(len(sets))]
+        cp_args = [rawcall.prepare(lib, "tk_copy_stream", (vsrc[i].data_ptr(), vdst[i].data_ptr(), half, sh),
+                                   {"src": vsrc[i], "dst": vdst[i]})[1] for i in range(len(sets))]
+
+        def timed(step_i):
+            count = [0]
+
+            def step():
+                step_i(count[0] % len(sets))
+                count[0] += 1
+            settle_clocks(step, stream, args.settle_ms)
+            for _ in range(args.warmup):
+                step()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / args.steps
+        hip_us = timed(lambda i: vdst[i].copy_(vsrc[i]))
+        own_us = timed(lambda i: lib.tk_copy_stream(*cp_args[i]))
+        if not torch.equal(vdst[0], vsrc[0]):
+            raise SystemExit("copy check failed")
+        vendor = {"bytes_each_way": half, "hip_memcpy_us": round(hip_us, 3), "tk_copy_stream_us": round(own_us, 3),
+                  "hip_memcpy_gbs": round(2 * half / hip_us / 1e3, 2),
+                  "tk_copy_stream_gbs": round(2 * half / own_us / 1e3, 2)}
+        del vsrc, vdst
+
     ms_per_step = span_ms / args.steps
     value = nbytes * args.steps / (span_ms / 1e3) / 1e9
     avg_launch_ms = ms_per_step
@@ -592,6 +640,7 @@ def main():
             "op_frac_of_ceiling": round(ceil_us / ms_per_step / 1e3, 4),
         },
         "flushed": flushed,
+        **({"vendor_copy": vendor} if vendor is not None else {}),
     }
     if args.calibrate_copy:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
