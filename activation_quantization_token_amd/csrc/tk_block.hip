@@ -562,6 +562,7 @@ tk_status validate_common(const void *x, int64_t rows, int64_t cols, int64_t x_l
     const int64_t q_cols = (out_dtype == kE4M3) ? cols : cols / 2;
     if (x_ld < cols || q_ld < q_cols) return TK_ERROR_INVALID_VALUE;
     if (cols >= (int64_t(1) << 29)) return TK_ERROR_UNSUPPORTED;   // row byte offsets are 32-bit
+    if (!span_ok(rows, x_ld, cols, 2) || !span_ok(rows, q_ld, q_cols, 1)) return TK_ERROR_INVALID_VALUE;
     if (rows == 0) return TK_SUCCESS;
     if (!x || !q || !scales) return TK_ERROR_INVALID_VALUE;
     if (!aligned(x, 16) || (x_ld * 2) % 16 != 0) return TK_ERROR_MISALIGNED;
@@ -688,6 +689,7 @@ tk_status tk_per_block_cast(const void *x, int64_t rows, int64_t cols, int64_t x
     tk_status st = validate_common(x, rows, cols, x_ld, q, q_ld, scales, out_dtype, round_pow2, scale_fmt);
     if (st != TK_SUCCESS || rows == 0) return st;
     if (block_rows > kMaxBlockRows) return TK_ERROR_UNSUPPORTED;
+    if (!span_ok((rows + block_rows - 1) / block_rows, s_ld, s_cols, 4)) return TK_ERROR_INVALID_VALUE;
     if (!aligned(scales, 4)) return TK_ERROR_MISALIGNED;
     // Blocks of one row are the per-token groups: same layouts, same values.
     if (block_rows == 1)
@@ -720,7 +722,7 @@ tk_status tk_per_block_cast(const void *x, int64_t rows, int64_t cols, int64_t x
 
 int64_t tk_per_channel_workspace_bytes(int64_t rows, int64_t cols)
 {
-    if (rows <= 0 || cols <= 0) return 0;
+    if (rows <= 0 || cols <= 0 || rows > kMaxSpanBytes || cols >= (int64_t(1) << 29)) return 0;
     return channel_workspace_bytes(rows, cols);
 }
 

@@ -46,6 +46,20 @@ tk_status device_info(int *dev_out, DeviceInfo **info_out)
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Largest span accepted for an operand, (rows - 1) * ld + row length, in
+// bytes: far beyond any device's memory, and small enough that every offset
+// the host and the kernels form from rows, strides and sizes fits in int64.
+constexpr int64_t kMaxSpanBytes = int64_t(1) << 52;
+
+// Whether a [rows, row_elems] operand of elem-byte elements with a row stride
+// of ld elements (ld >= row_elems >= 1) spans at most kMaxSpanBytes.
+inline bool span_ok(int64_t rows, int64_t ld, int64_t row_elems, int64_t elem)
+{
+    if (rows <= 0) return true;
+    const int64_t lim = kMaxSpanBytes / elem;
+    return ld <= lim && rows - 1 <= (lim - row_elems) / ld;
+}
+
 // Run length (log2 of items) of xcd_order for a grid of `grid` workgroups
 // over n items, each workgroup reading item_bytes of input: runs of about
 // 1 MiB of input per XCD, 512 KiB when the whole input is at most 56 MiB
@@ -58,24 +72,17 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // cast-and-cast-back (-1.2 % at 32768 rows) and the stream ceiling use it;
 // RMSNorm, per-block, per-channel and dequantization measured no gain (or a
 // loss) and keep their order.
-#ifndef TK_XCD_RUN_SHIFT
-#define TK_XCD_RUN_SHIFT 0
-#endif
 constexpr int64_t kXcdRunBytes = int64_t(1) << 20;
 constexpr int64_t kXcdSmallRunBytes = int64_t(1) << 19;
 constexpr int64_t kXcdSmallInputBytes = int64_t(4096) * 7168 * 2;
 
 inline int xcd_run_log2(int64_t n, int64_t grid, int64_t item_bytes)
 {
-#ifdef TK_XCD_OFF
-    return -1;
-#endif
     if (grid != n || item_bytes <= 0) return -1;
     const int64_t target = n * item_bytes <= kXcdSmallInputBytes ? kXcdSmallRunBytes : kXcdRunBytes;
     int L = 0;
     while (L < 12 && (item_bytes << (L + 1)) <= target) ++L;
-    L += TK_XCD_RUN_SHIFT;
-    return L < 0 ? 0 : L;
+    return L;
 }
 
 }  // namespace

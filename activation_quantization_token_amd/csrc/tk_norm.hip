@@ -645,6 +645,7 @@ tk_status validate_norm(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
     if (rows < 0 || cols <= 0 || x_ld < cols) return TK_ERROR_INVALID_VALUE;
     if (!(eps > 0.0f) || !(eps <= FLT_MAX)) return TK_ERROR_INVALID_VALUE;
     if (cols > kNormMaxCols) return TK_ERROR_UNSUPPORTED;
+    if (!span_ok(rows, x_ld, cols, 2)) return TK_ERROR_INVALID_VALUE;
     if (rows == 0) return TK_SUCCESS;
     if (!x) return TK_ERROR_INVALID_VALUE;
     if (!aligned(x, 16) || (x_ld * 2) % 16 != 0 || (weight && !aligned(weight, 16))) return TK_ERROR_MISALIGNED;
@@ -710,6 +711,7 @@ tk_status tk_rmsnorm(const void *x, int64_t rows, int64_t cols, int64_t x_ld, co
     if (st != TK_SUCCESS || rows == 0) return st;
     if (!y) return TK_ERROR_INVALID_VALUE;
     const int64_t ysize = y_dtype == TK_OUT_F32 ? 4 : 2;
+    if (!span_ok(rows, y_ld, cols, ysize)) return TK_ERROR_INVALID_VALUE;
     if (!aligned(y, 16) || (y_ld * ysize) % 16 != 0) return TK_ERROR_MISALIGNED;
     int dev = 0;
     DeviceInfo *info = nullptr;
@@ -736,6 +738,7 @@ tk_status tk_rmsnorm_cast(const void *x, int64_t rows, int64_t cols, int64_t x_l
     if (q_ld < q_cols || s_ld < s_cols) return TK_ERROR_INVALID_VALUE;
     tk_status st = validate_norm(x, rows, cols, x_ld, weight, eps);
     if (st != TK_SUCCESS || rows == 0) return st;
+    if (!span_ok(rows, q_ld, q_cols, 1) || !span_ok(rows, s_ld, s_cols, 4)) return TK_ERROR_INVALID_VALUE;
     if (!q || !scales) return TK_ERROR_INVALID_VALUE;
     const int64_t qa = out_dtype == kE4M3 ? 8 : 4;
     if (!aligned(q, uintptr_t(qa)) || q_ld % qa != 0 || !aligned(scales, 4)) return TK_ERROR_MISALIGNED;

@@ -683,6 +683,8 @@ tk_status validate(const void *x, int64_t rows, int64_t cols, int64_t x_ld, void
     const int64_t s_cols = (scale_fmt == kScaleF32) ? ngroups : ngroups / 4;
     if (x_ld < in_cols || q_ld < q_cols || s_ld < s_cols) return TK_ERROR_INVALID_VALUE;
     if (in_cols >= (int64_t(1) << 29)) return TK_ERROR_UNSUPPORTED;   // row byte offsets are 32-bit
+    if (!span_ok(rows, x_ld, in_cols, 2) || !span_ok(rows, q_ld, q_cols, 1) || !span_ok(rows, s_ld, s_cols, 4))
+        return TK_ERROR_INVALID_VALUE;
     if (rows == 0) return TK_SUCCESS;
     if (!x || !q || !scales) return TK_ERROR_INVALID_VALUE;
     if (!aligned(x, 16) || (x_ld * 2) % 16 != 0) return TK_ERROR_MISALIGNED;
@@ -976,6 +978,7 @@ tk_status tk_per_token_cast_f32(const void *x, int64_t rows, int64_t cols, int64
                                                                                    : TK_SUCCESS;
     }
     if (st != TK_SUCCESS || rows == 0) return st;
+    if (!span_ok(rows, x_ld, cols, 4)) return TK_ERROR_INVALID_VALUE;
     if (!aligned(x, 16) || (x_ld * 4) % 16 != 0) return TK_ERROR_MISALIGNED;
     const int64_t s_words = scale_fmt == kScaleF32 ? cols / group : cols / group / 4;
     if (s_words * 4 > kRowScaleLdsBytes) return TK_ERROR_UNSUPPORTED;
@@ -1019,6 +1022,7 @@ tk_status tk_per_token_cast_back(const void *x, int64_t rows, int64_t cols, int6
     if (rows < 0 || cols <= 0 || cols % group != 0) return TK_ERROR_INVALID_VALUE;
     if (x_ld < cols || y_ld < cols) return TK_ERROR_INVALID_VALUE;
     if (cols >= (int64_t(1) << 29)) return TK_ERROR_UNSUPPORTED;
+    if (!span_ok(rows, x_ld, cols, 2) || !span_ok(rows, y_ld, cols, 2)) return TK_ERROR_INVALID_VALUE;
     if (rows == 0) return TK_SUCCESS;
     if (!x || !y) return TK_ERROR_INVALID_VALUE;
     if (!aligned(x, 16) || (x_ld * 2) % 16 != 0 || !aligned(y, 16) || (y_ld * 2) % 16 != 0)
@@ -1048,10 +1052,12 @@ tk_status tk_per_token_dequant(const void *q, int64_t rows, int64_t cols, int64_
     const int64_t s_cols = (scale_fmt == kScaleF32) ? ngroups : ngroups / 4;
     if (q_ld < q_cols || s_ld < s_cols || y_ld < cols) return TK_ERROR_INVALID_VALUE;
     if (cols >= (int64_t(1) << 29)) return TK_ERROR_UNSUPPORTED;
+    const int64_t ysize = (y_dtype == TK_OUT_F32) ? 4 : 2;
+    if (!span_ok(rows, q_ld, q_cols, 1) || !span_ok(rows, s_ld, s_cols, 4) || !span_ok(rows, y_ld, cols, ysize))
+        return TK_ERROR_INVALID_VALUE;
     if (rows == 0) return TK_SUCCESS;
     if (!q || !scales || !y) return TK_ERROR_INVALID_VALUE;
     const int64_t qa = (in_dtype == kE4M3) ? 8 : 4;
-    const int64_t ysize = (y_dtype == TK_OUT_F32) ? 4 : 2;
     if (!aligned(q, uintptr_t(qa)) || q_ld % qa != 0 || !aligned(scales, 4) || !aligned(y, 16) ||
         (y_ld * ysize) % 16 != 0)
         return TK_ERROR_MISALIGNED;
@@ -1068,7 +1074,7 @@ tk_status tk_per_token_dequant(const void *q, int64_t rows, int64_t cols, int64_
 
 tk_status tk_silu32_bf16(const void *g, void *out, int64_t n, void *stream)
 {
-    if (n < 0) return TK_ERROR_INVALID_VALUE;
+    if (n < 0 || n > kMaxSpanBytes / 4) return TK_ERROR_INVALID_VALUE;
     if (n == 0) return TK_SUCCESS;
     if (!g || !out) return TK_ERROR_INVALID_VALUE;
     if (!aligned(g, 2) || !aligned(out, 4)) return TK_ERROR_MISALIGNED;

@@ -38,7 +38,10 @@
  * stream) and return without waiting; outputs are valid once the stream
  * reaches that point.  The library allocates no per-call memory.  All
  * argument checks run on the host before anything is enqueued: on error
- * nothing is launched and the outputs are untouched.  Inputs with NaN or Inf,
+ * nothing is launched and the outputs are untouched.  Each operand's span,
+ * (rows - 1) * row stride + row length in bytes, must be at most 2^52 bytes
+ * (TK_ERROR_INVALID_VALUE otherwise: no device holds that much, and the
+ * limit keeps every offset the library forms inside int64).  Inputs with NaN or Inf,
  * and SwiGLU inputs whose product silu(gate) * up overflows fp32, give
  * unspecified codes and scales (outside the contract; no fault).
  */
@@ -213,6 +216,8 @@ tk_status tk_per_block_cast(const void *x, int64_t rows, int64_t cols, int64_t x
  * between the two passes).  The workspace holds the column maxima of up to
  * 32 row chunks and then the column scales.  Errors as for tk_per_token_cast;
  * a missing or short workspace is TK_ERROR_INVALID_VALUE.
+ * tk_per_channel_workspace_bytes returns 0 for rows or cols <= 0 and for sizes
+ * the cast refuses whatever the strides (rows above 2^52, cols from 2^29).
  */
 int64_t tk_per_channel_workspace_bytes(int64_t rows, int64_t cols);
 tk_status tk_per_channel_cast(const void *x, int64_t rows, int64_t cols, int64_t x_ld,
@@ -280,7 +285,7 @@ tk_status tk_rmsnorm_cast(const void *x, int64_t rows, int64_t cols, int64_t x_l
  * tk_silu32_bf16 -- diagnostic: out[i] = silu32(g[i]) for n bf16 gates, by the
  * same device lookup that tk_swiglu_per_token_cast uses for its gate half
  * (fp32 nearest to g / (1 + e^-g)).  g: bf16 [n] (2-byte aligned), out: fp32
- * [n] (4-byte aligned), both device pointers; n >= 0.  Asynchronous on
+ * [n] (4-byte aligned), both device pointers; 0 <= n <= 2^50.  Asynchronous on
  * `stream` after the first call on a device (see tk_swiglu_per_token_cast).
  */
 tk_status tk_silu32_bf16(const void *g, void *out, int64_t n, void *stream);

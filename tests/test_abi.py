@@ -90,6 +90,11 @@ def call(fn=tk.tk_per_token_cast, x=X, rows=4, cols=256, x_ld=None, q=Q, q_ld=No
     (dict(s=S + 2), MISALIGNED),
     (dict(x_ld=260, cols=256), MISALIGNED),          # 520-byte rows: not 16-byte multiples
     (dict(q_ld=260), MISALIGNED),
+    (dict(rows=1 << 62), INVALID),                   # spans beyond 2^52 bytes
+    (dict(rows=1 << 45), INVALID),
+    (dict(x_ld=1 << 61), INVALID),
+    (dict(q_ld=1 << 60), INVALID),
+    (dict(s_ld=1 << 60), INVALID),
 ])
 def test_validation_errors(fn, swiglu, kw, want):
     if swiglu and "x_ld" in kw:
@@ -101,6 +106,7 @@ def test_validation_errors(fn, swiglu, kw, want):
 def test_zero_rows_is_a_no_op(fn, swiglu):
     # rows == 0 succeeds without touching (null) pointers or the device
     assert call(fn, rows=0, x=0, q=0, s=0, swiglu=swiglu) == 0
+    assert call(fn, rows=0, x=0, q=0, s=0, x_ld=1 << 62, q_ld=1 << 62, s_ld=1 << 62, swiglu=swiglu) == 0
 
 
 def test_silu_diagnostic_validation():
@@ -109,6 +115,8 @@ def test_silu_diagnostic_validation():
     assert tk.tk_silu32_bf16(0, Q, 5, 0) == INVALID
     assert tk.tk_silu32_bf16(X + 1, Q, 5, 0) == MISALIGNED
     assert tk.tk_silu32_bf16(X, Q + 2, 5, 0) == MISALIGNED
+    assert tk.tk_silu32_bf16(X, Q, 1 << 62, 0) == INVALID
+    assert tk.tk_silu32_bf16(X, Q, (1 << 63) - 1, 0) == INVALID
 
 
 Y = 0x40000
@@ -121,6 +129,8 @@ Y = 0x40000
     (dict(y_ld=100), INVALID), (dict(q=0), INVALID), (dict(y=0), INVALID), (dict(s=0), INVALID),
     (dict(q=Q + 4), MISALIGNED), (dict(y=Y + 8), MISALIGNED), (dict(s=S + 2), MISALIGNED),
     (dict(y_ld=260), MISALIGNED), (dict(rows=0, q=0, s=0, y=0), 0),
+    (dict(rows=1 << 62), INVALID), (dict(q_ld=1 << 60), INVALID), (dict(s_ld=1 << 60), INVALID),
+    (dict(y_ld=1 << 60), INVALID), (dict(rows=0, q=0, s=0, y=0, q_ld=1 << 62, y_ld=1 << 62), 0),
 ])
 def test_dequant_validation(kw, want):
     a = dict(q=Q, rows=4, cols=256, q_ld=None, s=S, s_ld=None, group=32, in_dtype=0, scale_fmt=0, y=Y,
@@ -138,6 +148,7 @@ def test_dequant_validation(kw, want):
     (dict(x_ld=100), INVALID), (dict(y_ld=100), INVALID), (dict(x=0), INVALID), (dict(y=0), INVALID),
     (dict(x=X + 8), MISALIGNED), (dict(y=Y + 8), MISALIGNED), (dict(y_ld=260), MISALIGNED),
     (dict(rows=0, x=0, y=0), 0),
+    (dict(rows=1 << 62), INVALID), (dict(x_ld=1 << 61), INVALID), (dict(y_ld=1 << 61), INVALID),
 ])
 def test_cast_back_validation(kw, want):
     a = dict(x=X, rows=4, cols=256, x_ld=256, y=Y, y_ld=256, group=32, out_dtype=0, round_pow2=1)
@@ -151,6 +162,8 @@ def test_cast_back_validation(kw, want):
     (dict(scale_fmt=1, round_pow2=0), INVALID), (dict(x=X + 8), MISALIGNED), (dict(x_ld=258), MISALIGNED),
     (dict(q=Q + 4), MISALIGNED), (dict(rows=0, x=0, q=0, s=0), 0),
     (dict(group=16, cols=16 * 8200, x_ld=16 * 8200, q_ld=16 * 8200, s_ld=8200), UNSUPPORTED),
+    (dict(rows=1 << 62), INVALID), (dict(x_ld=1 << 61), INVALID), (dict(x_ld=1 << 50), INVALID),   # 2^52 B rows
+    (dict(q_ld=1 << 60), INVALID), (dict(s_ld=1 << 60), INVALID),
 ])
 def test_cast_f32_validation(kw, want):
     a = dict(x=X, rows=4, cols=256, x_ld=256, q=Q, q_ld=256, s=S, s_ld=8, group=32, out_dtype=0, round_pow2=1,
@@ -168,6 +181,8 @@ def test_cast_f32_validation(kw, want):
     (dict(x=0), INVALID), (dict(q=0), INVALID), (dict(s=0), INVALID),
     (dict(x=X + 8), MISALIGNED), (dict(x_ld=260), MISALIGNED), (dict(q=Q + 4), MISALIGNED),
     (dict(s=S + 2), MISALIGNED), (dict(block_rows=257), UNSUPPORTED), (dict(rows=0, x=0, q=0, s=0), 0),
+    (dict(rows=1 << 62), INVALID), (dict(x_ld=1 << 61), INVALID), (dict(q_ld=1 << 61), INVALID),
+    (dict(s_ld=1 << 60, rows=512), INVALID),
 ])
 def test_per_block_validation(kw, want):
     a = dict(x=X, rows=4, cols=256, x_ld=256, q=Q, q_ld=256, s=S, s_ld=8, block_rows=128, block_cols=32,
@@ -188,6 +203,7 @@ W = 0x50000
     (dict(ws_bytes=16), INVALID), (dict(x=X + 8), MISALIGNED), (dict(q=Q + 4), MISALIGNED),
     (dict(s=S + 8), MISALIGNED), (dict(ws=W + 8), MISALIGNED),
     (dict(rows=0, x=0, q=0, s=0, ws=0, ws_bytes=0), 0),
+    (dict(rows=1 << 62, ws_bytes=1 << 40), INVALID), (dict(x_ld=1 << 61), INVALID), (dict(q_ld=1 << 61), INVALID),
 ])
 def test_per_channel_validation(kw, want):
     a = dict(x=X, rows=4, cols=256, x_ld=256, q=Q, q_ld=256, s=S, ws=W, ws_bytes=None, out_dtype=0, round_pow2=1,
@@ -204,6 +220,7 @@ def test_per_channel_validation(kw, want):
     (dict(x=X + 8), MISALIGNED), (dict(s=S + 8), MISALIGNED),
     (dict(rows=4096, cols=16392, x_ld=16392, q_ld=16392), UNSUPPORTED),    # workspace above 1088 KiB
     (dict(rows=0, x=0, q=0, s=0), 0),
+    (dict(rows=1 << 62), INVALID), (dict(x_ld=1 << 61), INVALID),
 ])
 def test_per_channel_noalloc_validation(kw, want):
     """Checks before anything is launched (the valid calls here stop at the
@@ -232,6 +249,12 @@ def test_per_channel_workspace_size():
     assert tk.tk_per_channel_workspace_bytes(10**6, 16) <= _ws(32, 16)
     # the largest input the allocation-free entry point takes: 32 chunks of 16384 columns
     assert tk.tk_per_channel_workspace_bytes(4096, 16384) == binding.tk_per_channel_noalloc_max_workspace_bytes()
+    # sizes the cast refuses whatever the strides: no size, and no overflow
+    assert tk.tk_per_channel_workspace_bytes(1 << 52, 8) == _ws(32, 8)
+    assert tk.tk_per_channel_workspace_bytes((1 << 52) + 1, 8) == 0
+    assert tk.tk_per_channel_workspace_bytes((1 << 63) - 1, 8) == 0
+    assert tk.tk_per_channel_workspace_bytes(64, 1 << 29) == 0
+    assert tk.tk_per_channel_workspace_bytes((1 << 63) - 1, (1 << 63) - 1) == 0
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -240,6 +263,8 @@ def test_per_channel_workspace_size():
     (dict(eps=float("nan")), INVALID), (dict(y_dtype=2), INVALID), (dict(x=0), INVALID), (dict(y=0), INVALID),
     (dict(x=X + 8), MISALIGNED), (dict(y=Y + 8), MISALIGNED), (dict(w=W + 8), MISALIGNED), (dict(x_ld=260), MISALIGNED),
     (dict(cols=16392, x_ld=16392, y_ld=16392), UNSUPPORTED), (dict(rows=0, x=0, y=0), 0),
+    (dict(rows=1 << 62), INVALID), (dict(x_ld=1 << 61), INVALID), (dict(y_ld=1 << 61), INVALID),
+    (dict(y_ld=1 << 50, y_dtype=1), INVALID), (dict(rows=0, x=0, y=0, x_ld=1 << 62, y_ld=1 << 62), 0),
 ])
 def test_rmsnorm_validation(kw, want):
     a = dict(x=X, rows=4, cols=256, x_ld=256, w=W, eps=1e-6, y=Y, y_ld=256, y_dtype=0)
@@ -255,6 +280,8 @@ def test_rmsnorm_validation(kw, want):
     (dict(s=0), INVALID), (dict(x=X + 8), MISALIGNED), (dict(q=Q + 4), MISALIGNED), (dict(s=S + 2), MISALIGNED),
     (dict(w=W + 8), MISALIGNED), (dict(cols=16384 + 128, x_ld=16512, q_ld=16512, s_ld=516), UNSUPPORTED),
     (dict(rows=0, x=0, q=0, s=0), 0),
+    (dict(rows=1 << 62), INVALID), (dict(x_ld=1 << 61), INVALID), (dict(q_ld=1 << 61), INVALID),
+    (dict(s_ld=1 << 60), INVALID),
 ])
 def test_rmsnorm_cast_validation(kw, want):
     a = dict(x=X, rows=4, cols=256, x_ld=256, w=W, eps=1e-6, q=Q, q_ld=256, s=S, s_ld=8, group=32, out_dtype=0,
