@@ -324,8 +324,9 @@ __global__ __launch_bounds__(kWave * kNormMaxWaves) void rmsnorm_kernel(NormPara
 }
 
 // ---------------------------------------------------------------------------
-// One wave per row, for rows of up to 7168 channels.  Each wave of a 4-wave
-// workgroup converts its own rows (rows wave_id, wave_id + total waves, ...):
+// One wave per row, for rows of up to 7168 channels.  Each wave of a workgroup
+// of WPB waves (4, or 8 for the row counts chosen at launch) converts its own
+// rows (rows wave_id, wave_id + total waves, ...):
 // the row's NS 512-column segments stay in registers, the sum of squares needs
 // only the in-wave reduction, the per-row scalar work (certification,
 // division, square root, reciprocal) is spread over 8 NS values per lane, and
@@ -337,8 +338,8 @@ __global__ __launch_bounds__(kWave * kNormMaxWaves) void rmsnorm_kernel(NormPara
 // up to 8 NS = 112 squares in sequence: with the 6 shuffle levels that is at
 // most 118 roundings, within the 256-unit margin of certified().
 
-constexpr int kNormWaveWPB = 4;
 constexpr int kNormWaveWavesPerSIMD = 4;          // at most 128 VGPRs, so 16 waves fit on a CU
+constexpr int kNormWaveSlotsPerCU = 4 * kNormWaveWavesPerSIMD;
 
 // Exact sum of squares of one wave's row (its lanes' NS segments), rounded
 // to fp32; the arithmetic of exact_sum_squares, with the digits in this
@@ -508,13 +509,13 @@ __device__ __forceinline__ int64_t uniform64(int64_t v)
 // grid of 16 waves per CU whose waves load their next row into the registers
 // the cast frees: 7 % faster at 32768 x 7168, 2 % at 16384; storing each
 // segment's codes as it is converted: 9 % slower at 4096 x 7168.
-template <int G, int QD, bool POW2, int SF, int OUT, int NS>
-__global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void rmsnorm_wave_kernel(NormParams p)
+template <int G, int QD, bool POW2, int SF, int OUT, int NS, int WPB>
+__global__ __launch_bounds__(kWave * WPB, kNormWaveWavesPerSIMD) void rmsnorm_wave_kernel(NormParams p)
 {
     constexpr int kCols = NS * kSegCols;
     extern __shared__ float lds_weight[];                                 // fp32 [NS * 512]
-    __shared__ uint32_t stage[kNormWaveWPB][kCols / 16];
-    __shared__ unsigned long long exact_acc[kNormWaveWPB][kExactDigits];
+    __shared__ uint32_t stage[WPB][kCols / 16];
+    __shared__ unsigned long long exact_acc[WPB][kExactDigits];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t cols = uint32_t(p.cols);
@@ -523,8 +524,8 @@ __global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void r
     // Segment k of a lane is byte lane * 16 + k * 1024 of the row, the
     // segment offset in the instruction's scalar offset.  The first row's
     // loads go out before the weight row is staged.
-    const int64_t nwaves = int64_t(gridDim.x) * kNormWaveWPB;
-    int64_t row = uniform64(int64_t(blockIdx.x) * kNormWaveWPB + wave);
+    const int64_t nwaves = int64_t(gridDim.x) * WPB;
+    int64_t row = uniform64(int64_t(blockIdx.x) * WPB + wave);
     const uint32_t q_bytes = QD == kE4M3 ? cols : cols / 2;
     u32x4 xs[NS];
     auto load_row = [&](int64_t r) {
@@ -540,18 +541,18 @@ __global__ __launch_bounds__(kWave * kNormWaveWPB, kNormWaveWavesPerSIMD) void r
     // pieces that are all in flight at once.
     {
         constexpr int kPieces = kCols / 8;                                  // 8 weights each
-        constexpr int kPerThread = (kPieces + kWave * kNormWaveWPB - 1) / (kWave * kNormWaveWPB);
+        constexpr int kPerThread = (kPieces + kWave * WPB - 1) / (kWave * WPB);
         u32x4 wraw[kPerThread];
         const __amdgpu_buffer_rsrc_t wrow = row_buffer(p.w, p.w ? cols * 2u : 0u);
 #pragma unroll
         for (int c = 0; c < kPerThread; ++c)
-            wraw[c] = __builtin_amdgcn_raw_buffer_load_b128(wrow, int((threadIdx.x + c * kWave * kNormWaveWPB) * 16u),
+            wraw[c] = __builtin_amdgcn_raw_buffer_load_b128(wrow, int((threadIdx.x + c * kWave * WPB) * 16u),
                                                             0, 0);
         typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int c = 0; c < kPerThread; ++c) {
-            const uint32_t piece = threadIdx.x + c * kWave * kNormWaveWPB;
-            if (kPieces % (kWave * kNormWaveWPB) == 0 || piece < uint32_t(kPieces)) {
+            const uint32_t piece = threadIdx.x + c * kWave * WPB;
+            if (kPieces % (kWave * WPB) == 0 || piece < uint32_t(kPieces)) {
                 float f[8];
                 widen8(wraw[c], f);
                 if (!p.w) {
@@ -602,15 +603,18 @@ constexpr int kWaveNS[3] = {4, 8, 14};
 struct NormTable {
     NormFn cast[4][4][2][3];     // [kernel: workgroup, one wave per row with NS 4/8/14][group][code format][variant]
     NormFn plain[4][2];          // [the same kernels][bf16 y, fp32 y]
+    NormFn cast8[4][2][3];       // NS 14 in workgroups of 8 waves: [group][code format][variant]
+    NormFn plain8[2];
 };
 
 template <int G, int QD, bool POW2, int SF>
 void fill_norm_variant(NormTable &t, int gi, int vi)
 {
     t.cast[0][gi][QD][vi] = rmsnorm_kernel<G, QD, POW2, SF, kOutCast>;
-    t.cast[1][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 4>;
-    t.cast[2][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 8>;
-    t.cast[3][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 14>;
+    t.cast[1][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 4, 4>;
+    t.cast[2][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 8, 4>;
+    t.cast[3][gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 14, 4>;
+    t.cast8[gi][QD][vi] = rmsnorm_wave_kernel<G, QD, POW2, SF, kOutCast, 14, 8>;
 }
 
 template <int G, int QD>
@@ -631,12 +635,14 @@ NormTable make_norm_table()
     fill_norm<128, kE4M3>(t, 3); fill_norm<128, kE2M1>(t, 3);
     t.plain[0][0] = rmsnorm_kernel<16, kE4M3, false, kScaleF32, kOutBF16>;
     t.plain[0][1] = rmsnorm_kernel<16, kE4M3, false, kScaleF32, kOutF32>;
-    t.plain[1][0] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutBF16, 4>;
-    t.plain[1][1] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutF32, 4>;
-    t.plain[2][0] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutBF16, 8>;
-    t.plain[2][1] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutF32, 8>;
-    t.plain[3][0] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutBF16, 14>;
-    t.plain[3][1] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutF32, 14>;
+    t.plain[1][0] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutBF16, 4, 4>;
+    t.plain[1][1] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutF32, 4, 4>;
+    t.plain[2][0] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutBF16, 8, 4>;
+    t.plain[2][1] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutF32, 8, 4>;
+    t.plain[3][0] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutBF16, 14, 4>;
+    t.plain[3][1] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutF32, 14, 4>;
+    t.plain8[0] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutBF16, 14, 8>;
+    t.plain8[1] = rmsnorm_wave_kernel<16, kE4M3, false, kScaleF32, kOutF32, 14, 8>;
     return t;
 }
 
@@ -675,11 +681,25 @@ tk_status launch_norm(const NormTable &t, int gi, int qd, int variant, int plain
     // wider rows: one workgroup per row.
     const int ki = norm_kernel_index(p.cols);
     if (ki > 0) {
-        int64_t blocks = (p.rows + kNormWaveWPB - 1) / kNormWaveWPB;    // a wave for every row
+        // Workgroups of 4 waves, or of 8 for rows of 4097 to 7168 channels
+        // when the rows fill between three and four of each SIMD's four wave
+        // slots in one round (3072 < rows <= 4096 on 256 CUs): measured on
+        // MI355X at 7168 channels, 4-wave workgroups take 2.8 us longer for
+        // 3136 rows than for 3072 (13.3 -> 16.1 us), where 8-wave ones take
+        // 14.2 us; across that range 8 waves were 3-16 % faster for every
+        // code format, fp32 and UE8M0 scales, 5120 channels and the plain
+        // forward (4096 x 7168 E4M3 G128: 18.0 -> 16.8 us; E2M1 G32 UE8M0
+        // equal), and 6-10 % slower at 3072 rows and below and 5-8 % above
+        // 4096, where whole 8-wave workgroups wait for free slots.
+        const int64_t slots = int64_t(cus) * kNormWaveSlotsPerCU;
+        const bool eight = ki == 3 && p.rows * 4 > slots * 3 && p.rows <= slots;
+        const int wpb = eight ? 8 : 4;
+        int64_t blocks = (p.rows + wpb - 1) / wpb;                       // a wave for every row
         if (blocks > int64_t(0x7FFFFFFF)) blocks = int64_t(0x7FFFFFFF);  // taller inputs loop
-        const NormFn fn = plain >= 0 ? t.plain[ki][plain] : t.cast[ki][gi][qd][variant];
+        const NormFn fn = eight ? (plain >= 0 ? t.plain8[plain] : t.cast8[gi][qd][variant])
+                                : (plain >= 0 ? t.plain[ki][plain] : t.cast[ki][gi][qd][variant]);
         const size_t lds = size_t(kWaveNS[ki - 1]) * kSegCols * 4u;      // fp32 weight row
-        if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * kNormWaveWPB),
+        if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(uint32_t(blocks)), dim3(kWave * wpb),
                             args, lds, s) != hipSuccess)
             return TK_ERROR_LAUNCH;
         return TK_SUCCESS;

@@ -174,6 +174,31 @@ def test_rmsnorm_workgroup_kernel_loops_over_rows(cols):
     check_norm(x, _weight(3, cols), 1e-6, "bf16", label="workgroup kernel, tall")
 
 
+def _one_round_rows():
+    """Row counts around the band where rows of 4097..7168 channels run in
+    8-wave workgroups: more than three and at most four of the 16 wave slots
+    of every CU (3072 < rows <= 4096 on 256 CUs), plus both edges."""
+    slots = torch.cuda.get_device_properties(0).multi_processor_count * 16
+    return [3 * slots // 4, 3 * slots // 4 + 1, slots - 3, slots, slots + 1]
+
+
+@pytest.mark.parametrize("cols", [7168, 4224])
+@pytest.mark.parametrize("at", range(5))
+def test_rmsnorm_one_round_workgroup_sizes(cols, at):
+    """Both workgroup sizes of the one-wave-per-row kernel, on either side of
+    the band's edges (ragged last workgroups included), fused cast and plain
+    forward, with a strided input."""
+    rows = _one_round_rows()[at]
+    x = inputs.generate_small(40 + at, rows, cols, "student_t3")
+    w = _weight(7, cols)
+    if cols == 7168:
+        check_norm_cast(x, w, 1e-6, 128, "e4m3", True, "f32", label=f"one round, {rows} rows")
+        check_norm(x, w, 1e-6, "bf16", x_ld=cols + 8, label=f"one round, {rows} rows")
+    else:
+        check_norm_cast(x, w, 1e-5, 32, "e2m1", True, "ue8m0", x_ld=cols + 8, label=f"one round, {rows} rows")
+        check_norm(x, None, 1e-6, "f32", label=f"one round, {rows} rows")
+
+
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("cols", [1024, 3584, 7168])
 def test_rmsnorm_tall_inputs(out, cols):
