@@ -686,11 +686,12 @@ tk_status launch_norm(const NormTable &t, int gi, int qd, int variant, int plain
         // slots in one round (3072 < rows <= 4096 on 256 CUs): measured on
         // MI355X at 7168 channels, 4-wave workgroups take 2.8 us longer for
         // 3136 rows than for 3072 (13.3 -> 16.1 us), where 8-wave ones take
-        // 14.2 us; across that range 8 waves were 3-16 % faster for every
+        // 14.2 us; across that range 8 waves were 2-16 % faster for every
         // code format, fp32 and UE8M0 scales, 5120 channels and the plain
         // forward (4096 x 7168 E4M3 G128: 18.0 -> 16.8 us; E2M1 G32 UE8M0
-        // equal), and 6-10 % slower at 3072 rows and below and 5-8 % above
-        // 4096, where whole 8-wave workgroups wait for free slots.
+        // equal), and 4-16 % slower at 1024-3072 rows, 8 % just above 4096
+        // (whole 8-wave workgroups waiting for free slots) and 3-6 % at
+        // 8192-32768 rows.
         const int64_t slots = int64_t(cus) * kNormWaveSlotsPerCU;
         const bool eight = ki == 3 && p.rows * 4 > slots * 3 && p.rows <= slots;
         const int wpb = eight ? 8 : 4;
