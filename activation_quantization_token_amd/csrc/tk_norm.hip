@@ -523,7 +523,16 @@ __global__ __launch_bounds__(kWave * WPB, kNormWaveWavesPerSIMD) void rmsnorm_wa
 
     // Segment k of a lane is byte lane * 16 + k * 1024 of the row, the
     // segment offset in the instruction's scalar offset.  The first row's
-    // loads go out before the weight row is staged.
+    // loads go out together with the weight pieces that this thread stages:
+    // in 4-wave workgroups after them, so that the barrier below waits for the
+    // weight pieces alone and each wave starts on its row as soon as the row
+    // is in; in 8-wave workgroups (the one-round band chosen at launch) before
+    // them, so that the barrier waits for the workgroup's rows too.  Measured
+    // on MI355X against rows first for both: weight pieces first 2-6 % faster
+    // at 4096 to 32768 rows of 7168 channels, 11-19 % at 256 to 2560 rows,
+    // 6-14 % at 4096 channels; 1.7 % slower at exactly 3072 x 7168 and 3 % at
+    // 6144 x 2048 (grids of exactly one round), and 1-4 % slower in the 8-wave
+    // band.
     const int64_t nwaves = int64_t(gridDim.x) * WPB;
     int64_t row = uniform64(int64_t(blockIdx.x) * WPB + wave);
     const uint32_t q_bytes = QD == kE4M3 ? cols : cols / 2;
@@ -534,7 +543,10 @@ __global__ __launch_bounds__(kWave * WPB, kNormWaveWavesPerSIMD) void rmsnorm_wa
         for (int k = 0; k < NS; ++k)
             xs[k] = __builtin_amdgcn_raw_buffer_load_b128(xrow, int(lane * 16), k * kSegCols * 2, kNonTemporal);
     };
-    if (row < p.rows) load_row(row);
+    constexpr bool kWeightFirst = WPB == 4;
+    if constexpr (!kWeightFirst) {
+        if (row < p.rows) load_row(row);
+    }
 
     // Weight row into LDS as fp32 (w_j, or 1.0 without a weight; 0 past the
     // row end) in the layout of weight_slot, read from memory in 16-byte
@@ -548,6 +560,20 @@ __global__ __launch_bounds__(kWave * WPB, kNormWaveWavesPerSIMD) void rmsnorm_wa
         for (int c = 0; c < kPerThread; ++c)
             wraw[c] = __builtin_amdgcn_raw_buffer_load_b128(wrow, int((threadIdx.x + c * kWave * WPB) * 16u),
                                                             0, 0);
+        if constexpr (kWeightFirst) {
+            // Issued after the weight pieces whatever the compiler's schedule,
+            // and without a branch (a wave without a row reads nothing through
+            // an empty descriptor), so that the wait for the weight pieces
+            // leaves the row's loads in flight.
+            __builtin_amdgcn_sched_barrier(0);
+            const bool valid = row < p.rows;
+            const __amdgpu_buffer_rsrc_t xrow =
+                row_buffer(p.x + (valid ? row : 0) * p.x_ld, valid ? cols * 2u : 0u);
+#pragma unroll
+            for (int k = 0; k < NS; ++k)
+                xs[k] = __builtin_amdgcn_raw_buffer_load_b128(xrow, int(lane * 16), k * kSegCols * 2, kNonTemporal);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int c = 0; c < kPerThread; ++c) {
